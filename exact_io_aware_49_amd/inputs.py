@@ -1,0 +1,105 @@
+"""Seeded synthetic inputs and the workload table.
+
+This module is shared by the GPU path's tests/benchmark and by the oracle's
+tests.  It holds no attention arithmetic: it only draws numbers and rounds
+float32 values to bfloat16 (round to nearest, ties to even), the storage
+format the bf16 workloads hand to the kernels.
+
+Inputs are i.i.d. N(0, 1), drawn with numpy's PCG64 generator in the order
+Q, K, V, dO, each as a C-ordered [B, H, N, d] float32 array.  The pages'
+benchmarks ran on models and datasets (GPT-2, BERT-large, Long-Range Arena)
+that are not reproduced here; the workloads below borrow only their shapes:
+GPT-2-small self-attention (12 heads of 64, sequence 1K), a long-sequence
+encoder in the 1K-4K range, and a 32K-token long context.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str          # "fwd" or "bwd"
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str         # "f32" or "bf16"
+    scale: float
+    seed: int
+    note: str
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("fwd_f32_b1h2n128d64", "fwd", 1, 2, 128, 64, False, "f32", 1.0 / math.sqrt(64), 1,
+                 "small fp32 forward, non-causal"),
+        Workload("fwd_gpt2_causal_b8h12n1024d64", "fwd", 8, 12, 1024, 64, True, "bf16",
+                 1.0 / math.sqrt(64), 2, "GPT-2-small-shaped causal self-attention"),
+        Workload("fwd_encoder_b4h16n4096d128", "fwd", 4, 16, 4096, 128, False, "bf16",
+                 1.0 / math.sqrt(128), 3, "long-sequence encoder, non-causal"),
+        Workload("fwd_longctx_causal_b1h32n32768d128", "fwd", 1, 32, 32768, 128, True, "bf16",
+                 1.0 / math.sqrt(128), 4, "32K-token causal long context"),
+        Workload("bwd_causal_b4h16n2048d64", "bwd", 4, 16, 2048, 64, True, "bf16",
+                 1.0 / math.sqrt(64), 5, "causal backward with recomputation"),
+    ]
+}
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); return float32.
+
+    NaN stays NaN (quiet), +-Inf stays +-Inf, finite values beyond the bf16
+    range round to +-Inf as round-to-nearest-even prescribes.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    r = r.astype(np.uint32)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = (x.view(np.uint32)[nan] | np.uint32(0x00400000)) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def bf16_bits(x_bf16_valued: np.ndarray) -> np.ndarray:
+    """The uint16 storage of float32 values that are already bf16-representable."""
+    u = np.ascontiguousarray(x_bf16_valued, dtype=np.float32).view(np.uint32)
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def gen_tensors(shape, dtype: str, seed: int, count: int):
+    """`count` arrays of `shape`, i.i.d. N(0,1) float32 from PCG64(seed), in draw order.
+
+    For dtype "bf16" each array is rounded to bf16 values (still stored as float32).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(count):
+        a = rng.standard_normal(size=tuple(shape), dtype=np.float32)
+        if dtype == "bf16":
+            a = bf16_round(a)
+        out.append(a)
+    return out
+
+
+def gen_qkv(shape, dtype: str, seed: int, with_do: bool = False):
+    """Q, K, V (and dO) for one workload, drawn in that order."""
+    return gen_tensors(shape, dtype, seed, 4 if with_do else 3)
+
+
+def workload_inputs(w: Workload):
+    """Inputs of a named workload: Q, K, V (and dO for a backward workload)."""
+    return gen_qkv(w.shape, w.dtype, w.seed, with_do=(w.kind == "bwd"))

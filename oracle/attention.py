@@ -1,0 +1,201 @@
+"""Naive float64 attention and its gradients -- TEST INFRASTRUCTURE ONLY.
+
+The forward follows the attention equation of "FlashAttention (DE)",
+section "Problematik der Standard-Attention":
+
+    Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V
+
+computed the way that section describes the standard implementation: the
+whole N x N score matrix S is formed, each row is normalised by a two-pass
+softmax (row maximum, then exponentials and their sum), and the normalised
+matrix P multiplies V.  The scale 1/sqrt(d_k) is an argument (`scale`) so the
+caller can pass exactly the value the GPU receives.
+
+What the forward additionally returns, the per-row log-sum-exp
+lse_i = ln sum_j exp(S_ij), is the "small normalisation value" kept for the
+backward pass in the Dutch glossary page "FlashAttention", section
+"Hoe werkt het?", bullet "Herberekening".  The pages give no formula for it;
+the natural log of the row's exponential sum of the scaled scores is the
+plain reading.
+
+Masking is named among the fused steps in "FlashAttention (DE)", section
+"Zusammenfassen von Operationen in einem CUDA-Kernel", without a definition.
+The reading used here is the causal mask: query i sees key j iff j <= i
+(query and key positions both start at 0; N_q = N_k).  Masked scores are -inf
+and get probability exactly 0.
+
+The backward is the calculus of the attention equation for the scalar loss
+L = sum(dO * O); the pages give no backward equations:
+
+    dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
+    dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+
+All arithmetic is numpy float64 on the exact values the GPU receives (inputs
+are upcast, never rounded further).  Work is done one (batch, head) pair at a
+time; the row-chunked forward keeps whole rows of S (every key), so it is the
+same arithmetic with bounded memory.
+
+Layout: q, k, v, dO are [B, H, N, d]; lse is [B, H, N].
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale * q k^T for one head: q [Nq, d], k [Nk, d] -> [Nq, Nk] float64.
+
+    The product inside the softmax of the attention equation
+    ("FlashAttention (DE)", section "Problematik der Standard-Attention").
+    """
+    q64 = np.asarray(q, dtype=np.float64)
+    k64 = np.asarray(k, dtype=np.float64)
+    return float(scale) * (q64 @ k64.T)
+
+
+def causal_mask(s: np.ndarray, row_ids: np.ndarray) -> np.ndarray:
+    """Return a copy of S with S[r, j] = -inf wherever key j > query row_ids[r].
+
+    Causal reading of the masking step named in "FlashAttention (DE)",
+    section "Zusammenfassen von Operationen in einem CUDA-Kernel".
+    `row_ids` are the absolute query positions of the rows of S.
+    """
+    out = np.array(s, dtype=np.float64, copy=True)
+    cols = np.arange(out.shape[1])
+    hidden = cols[None, :] > np.asarray(row_ids)[:, None]
+    out[hidden] = -np.inf
+    return out
+
+
+def softmax_rows(s: np.ndarray):
+    """Two-pass softmax over each whole row of S.
+
+    Returns (P, m, l) with m_i = max_j S_ij, l_i = sum_j exp(S_ij - m_i) and
+    P_ij = exp(S_ij - m_i) / l_i.  A row that is entirely -inf (cannot occur
+    for the causal mask with N_q = N_k) gets P = 0, m = -inf, l = 0.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    m = np.max(s, axis=1)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    e = np.exp(s - m_safe[:, None])
+    e[~finite, :] = 0.0
+    l = np.sum(e, axis=1)
+    p = np.zeros_like(e)
+    p[finite] = e[finite] / l[finite, None]
+    return p, m, l
+
+
+def _lse(m: np.ndarray, l: np.ndarray) -> np.ndarray:
+    """lse_i = m_i + ln l_i (-inf for an empty row)."""
+    out = np.full(m.shape, -np.inf)
+    ok = l > 0
+    out[ok] = m[ok] + np.log(l[ok])
+    return out
+
+
+def _head_forward(q, k, v, causal: bool, scale: float, row_ids):
+    s = scores(q, k, scale)
+    if causal:
+        s = causal_mask(s, row_ids)
+    p, m, l = softmax_rows(s)
+    o = p @ np.asarray(v, dtype=np.float64)
+    return o, _lse(m, l)
+
+
+def attention_forward(q, k, v, causal: bool, scale: float, row_chunk: int | None = None):
+    """Exact attention forward.  q, k, v: [B, H, N, d] -> (O [B,H,N,d], lse [B,H,N]), float64.
+
+    With `row_chunk`, query rows are processed `row_chunk` at a time; each
+    chunk still sees every key, so the result is the same definition.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H, N, d = q.shape
+    if k.shape != (B, H, k.shape[2], d) or v.shape[:3] != k.shape[:3]:
+        raise ValueError("q, k, v shapes do not match")
+    o = np.empty((B, H, N, v.shape[3]), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    step = N if row_chunk is None else max(1, int(row_chunk))
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, step):
+                r1 = min(N, r0 + step)
+                rows = np.arange(r0, r1)
+                o[b, h, r0:r1], lse[b, h, r0:r1] = _head_forward(
+                    q[b, h, r0:r1], k[b, h], v[b, h], causal, scale, rows)
+    return o, lse
+
+
+def attention_forward_rows(q, k, v, causal: bool, scale: float, b: int, h: int, rows):
+    """Forward for selected query rows of one (b, h): -> (O rows [R, d], lse rows [R]).
+
+    Each output row depends only on its own row of S, so this is the same
+    definition evaluated at a sample of rows (used for spot checks at sizes
+    where the full matrix would not fit in host memory).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    return _head_forward(np.asarray(q)[b, h][rows], np.asarray(k)[b, h],
+                         np.asarray(v)[b, h], causal, scale, rows)
+
+
+def attention_probs(q, k, causal: bool, scale: float) -> np.ndarray:
+    """The full probability matrix P [B, H, N, N] (small inputs only)."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    B, H, N, _ = q.shape
+    p = np.empty((B, H, N, k.shape[2]), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = scores(q[b, h], k[b, h], scale)
+            if causal:
+                s = causal_mask(s, np.arange(N))
+            p[b, h] = softmax_rows(s)[0]
+    return p
+
+
+def attention_backward_from_probs(p, q, k, v, do, scale: float):
+    """Gradients of L = sum(dO * O) for one head, given that head's P.
+
+    dV = P^T dO; dP = dO V^T; D_i = sum_j P_ij dP_ij; dS = P (dP - D);
+    dQ = scale dS K; dK = scale dS^T Q.  All float64.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    dv = p.T @ do
+    dp = do @ v.T
+    dsum = np.sum(p * dp, axis=1)
+    ds = p * (dp - dsum[:, None])
+    dq = float(scale) * (ds @ k)
+    dk = float(scale) * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, causal: bool, scale: float):
+    """Exact attention backward: -> (dQ, dK, dV), each [B, H, N, d] float64.
+
+    P is formed from its definition (full S, two-pass softmax) for each head;
+    nothing from a forward pass on the GPU is used.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    do = np.asarray(do)
+    B, H, N, d = q.shape
+    dq = np.empty((B, H, N, d), dtype=np.float64)
+    dk = np.empty((B, H, k.shape[2], d), dtype=np.float64)
+    dv = np.empty((B, H, k.shape[2], v.shape[3]), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = scores(q[b, h], k[b, h], scale)
+            if causal:
+                s = causal_mask(s, np.arange(N))
+            p = softmax_rows(s)[0]
+            dq[b, h], dk[b, h], dv[b, h] = attention_backward_from_probs(
+                p, q[b, h], k[b, h], v[b, h], do[b, h], scale)
+    return dq, dk, dv

@@ -1,0 +1,62 @@
+"""Seeded input generation and the bf16 rounding used to build inputs (CPU only)."""
+
+import numpy as np
+import torch
+
+from exact_io_aware_49_amd import inputs
+
+
+def test_bf16_round_matches_torch():
+    r = np.random.Generator(np.random.PCG64(0))
+    x = np.concatenate([
+        r.standard_normal(100000).astype(np.float32),
+        (r.standard_normal(1000) * 1e38).astype(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, -3.3895314e38, 1e-40, -1e-40,
+                  1.00390625, 1.01171875, 1.0078125 + 2**-9], dtype=np.float32),
+    ])
+    # exact ties: mantissa bit patterns ending in 0x8000
+    # mantissa bits 16..22 random, bit 15 set, bits 0..14 clear; exponent fixed (finite values)
+    ties = ((r.integers(0, 2**7, 1000, dtype=np.uint32) << np.uint32(16)) | np.uint32(0x8000)
+            | np.uint32(0x3F800000)).view(np.float32)
+    x = np.concatenate([x, ties])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = inputs.bf16_round(x)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_bf16_round_nan_stays_nan():
+    x = np.array([np.nan, -np.nan], dtype=np.float32)
+    assert np.isnan(inputs.bf16_round(x)).all()
+
+
+def test_bf16_bits_roundtrip():
+    x = inputs.bf16_round(np.linspace(-5, 5, 1001, dtype=np.float32))
+    bits = inputs.bf16_bits(x)
+    back = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(back, x)
+
+
+def test_generation_is_seeded_and_ordered():
+    a = inputs.gen_qkv((1, 2, 8, 4), "f32", 7, with_do=True)
+    b = inputs.gen_qkv((1, 2, 8, 4), "f32", 7, with_do=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    rng = np.random.Generator(np.random.PCG64(7))
+    q = rng.standard_normal((1, 2, 8, 4), dtype=np.float32)
+    k = rng.standard_normal((1, 2, 8, 4), dtype=np.float32)
+    assert np.array_equal(a[0], q) and np.array_equal(a[1], k)
+
+
+def test_bf16_inputs_are_representable():
+    q, k, v = inputs.gen_qkv((1, 1, 64, 64), "bf16", 3)
+    for x in (q, k, v):
+        assert np.array_equal(inputs.bf16_round(x), x)
+
+
+def test_workload_table():
+    w = inputs.WORKLOADS
+    assert len(w) == 5
+    enc = w["fwd_encoder_b4h16n4096d128"]
+    assert enc.shape == (4, 16, 4096, 128) and not enc.causal and enc.dtype == "bf16"
+    assert abs(enc.scale - 128 ** -0.5) < 1e-15
+    assert w["bwd_causal_b4h16n2048d64"].kind == "bwd"
