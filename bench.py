@@ -1,0 +1,204 @@
+"""Benchmark: one training step of exact attention (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step runs the whole path once over one batch of synthetic inputs that are
+already resident in device memory: fa_fwd (O, lse) then fa_bwd (dQ, dK, dV,
+recomputing the score blocks from lse).  Workload: the non-causal
+long-sequence encoder shape B=4, H=16, N=4096, d=128 in bf16, inputs i.i.d.
+N(0,1) (seeded PCG64, rounded to bf16).
+
+Throughput counts 4*B*H*N^2*d flops for the forward (halved when causal) and
+2.5x that for the backward, i.e. the minimum matrix-product work; value =
+(forward + backward flops) / step time.  Per-kernel durations come from HIP
+events recorded on the stream the kernels run on.  The CPU baseline times the
+float64 oracle on a bounded sample of heads of the same workload.
+Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "fwd_encoder_b4h16n4096d128"
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the float64 oracle (forward + backward) on whole heads until ~budget_s elapse."""
+    import oracle
+    from exact_io_aware_49_amd import inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    B, H, N, d = w.shape
+    q, k, v, do = inputs.gen_qkv(w.shape, w.dtype, w.seed, with_do=True)
+    s = float(np.float32(w.scale))
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(B):
+        for h in range(H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            oracle.attention_forward(q[sl], k[sl], v[sl], w.causal, s)
+            oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], w.causal, s)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 3.5 * fwd_flops(1, heads, N, d, w.causal)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} of {B * H} heads (B={B},H={H},N={N},d={d}), float64 numpy forward+backward, "
+                  f"{dt:.1f} s wall",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    a = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every (batch, head) pair is "
+              "independent, so a multi-GPU run would shard heads with no communication). Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import exact_io_aware_49_amd as fa
+    from exact_io_aware_49_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    fa.load_library()
+    w = inputs.WORKLOADS[a.workload]
+    B, H, N, d = w.shape
+    causal = int(w.causal)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    q, k, v, do = (torch.from_numpy(x).to(dev).to(torch.bfloat16)
+                   for x in inputs.gen_qkv(w.shape, "bf16", w.seed, with_do=True))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws_bytes = fa.fa_bwd_workspace_size(B, H, N, d, fa.FA_DTYPE_BF16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    scale = float(w.scale)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def fwd():
+        rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                       causal, scale, fa.FA_DTYPE_BF16, sh)
+        if rc:
+            raise RuntimeError(fa.fa_status_string(rc))
+
+    def bwd():
+        rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N, d,
+                       causal, scale, fa.FA_DTYPE_BF16, sh)
+        if rc:
+            raise RuntimeError(fa.fa_status_string(rc))
+
+    for _ in range(a.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = wall * 1e3 / a.steps
+    ff = fwd_flops(B, H, N, d, w.causal)
+    bf = 2.5 * ff
+    value = (ff + bf) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = ff / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = bf / (bwd_ms * 1e-3) / 1e12
+
+    # dominant by time: the backward launch (two kernels) or the forward kernel
+    if bwd_ms >= fwd_ms:
+        dom = {"kernel": "fa_bwd (fa_bwd_dq_kernel + fa_bwd_dkdv_kernel)", "flops": bf, "ms": bwd_ms}
+    else:
+        dom = {"kernel": "fa_fwd_bf16_kernel", "flops": ff, "ms": fwd_ms}
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom["kernel"],
+                "avg_launch_ms": round(dom["ms"], 4)}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: i.i.d. N(0,1) from PCG64, rounded to bf16, resident in HBM",
+        "config": {"workload": w.name, "pass": "forward+backward", "B": B, "H": H, "N": N, "d": d,
+                   "causal": bool(w.causal), "scale": scale},
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(fwd_tf, 2),
+        "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+        "bwd_tflops": round(bwd_tf, 2),
+        "bwd_frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

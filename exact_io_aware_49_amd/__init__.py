@@ -1,0 +1,19 @@
+"""MI355X (gfx950) exact attention: fused tiled forward with online softmax and a
+recomputing backward, as hand-written HIP kernels behind the C ABI of
+include/fa.h (libfa.so).  Python here only marshals arguments.
+"""
+
+from .fa import (  # noqa: F401
+    FA_DTYPE_BF16,
+    FA_DTYPE_F32,
+    LIB_PATH,
+    backward,
+    default_scale,
+    fa_bwd,
+    fa_bwd_workspace_size,
+    fa_fwd,
+    fa_status_string,
+    fa_version,
+    forward,
+    load_library,
+)

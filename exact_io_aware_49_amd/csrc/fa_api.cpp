@@ -1,0 +1,95 @@
+// fa_api.cpp -- the C ABI of libfa.so: argument validation and dispatch.
+//
+// Every argument is checked before any HIP call, so a rejected call enqueues
+// nothing and touches no device state.  The launchers behind this layer live in
+// the .hip files; they report launch errors via hipGetLastError, mapped here to
+// FA_ERR_HIP.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int H, int N, int d, int causal, float scale, int dtype) {
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+  // B*H*N rows must stay below 2^55 (so B*H*N*d < 2^62), and the launch grids
+  // (at most one workgroup per 64 rows of each head) must fit in 2^31 - 1.
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > (1ull << 55) / (unsigned long long)N) return FA_ERR_BAD_SHAPE;
+  if (bh * (((unsigned long long)N + 63) / 64) > 0x7fffffffull) return FA_ERR_BAD_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_BAD_ARGUMENT;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_SCALE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char *fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H and N must be >= 1 and the tensor size must fit";
+    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM: head dim d must be 64 or 128";
+    case FA_ERR_UNSUPPORTED_DTYPE: return "FA_ERR_UNSUPPORTED_DTYPE: dtype not supported by this entry point";
+    case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite and > 0";
+    case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
+    case FA_ERR_WORKSPACE_TOO_SMALL: return "FA_ERR_WORKSPACE_TOO_SMALL: workspace missing or below fa_bwd_workspace_size()";
+    case FA_ERR_BAD_ARGUMENT: return "FA_ERR_BAD_ARGUMENT: causal must be 0 or 1";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch or runtime call failed";
+    default: return "unknown fa status code";
+  }
+}
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
+           int causal, float scale, int dtype, void *stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+  int st = check_common(B, H, N, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_MISALIGNED;
+  hipError_t e;
+  if (dtype == FA_DTYPE_BF16)
+    e = fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal == 1, scale, (hipStream_t)stream);
+  else
+    e = fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, causal == 1, scale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
+  if (check_common(B, H, N, d, 0, 1.0f, dtype) != FA_OK || dtype != FA_DTYPE_BF16) return 0;
+  const size_t bytes = (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+           void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes, int B, int H, int N, int d,
+           int causal, float scale, int dtype, void *stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
+  int st = check_common(B, H, N, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d, dtype);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  hipError_t e = fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, (float *)workspace, B, H, N, d,
+                                     causal == 1, scale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// fa_device.h -- device-side types and helpers shared by the gfx950 kernels.
+//
+// Matrix-core conventions (CDNA3/CDNA4 MFMA, wave64), used by every kernel:
+//   v_mfma_f32_32x32x16_bf16  C[32x32] += A[32x16] * B[16x32]
+//     A operand: lane l holds row (l % 32) and 8 consecutive k-slots of half (l / 32).
+//     B operand: lane l holds column (l % 32) and the same 8 k-slots.
+//     C/D      : lane l, register r holds C[row][col] with col = l % 32 and
+//                row = 8 * (r / 4) + 4 * (l / 32) + (r % 4).
+//   Which physical k each (half, slot) denotes does not matter as long as A and
+//   B use the same assignment, so kernels choose whatever k-order makes their
+//   loads contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+// 16-byte loads/stores.
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+__device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
+
+// Pack two floats into bf16 (round to nearest, ties to even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Eight floats -> bf16x8 operand.
+__device__ __forceinline__ bf16x8 to_bf16x8(float f0, float f1, float f2, float f3, float f4, float f5,
+                                            float f6, float f7) {
+  u32x4 u;
+  u[0] = pack_bf16x2(f0, f1);
+  u[1] = pack_bf16x2(f2, f3);
+  u[2] = pack_bf16x2(f4, f5);
+  u[3] = pack_bf16x2(f6, f7);
+  return as_bf16x8(u);
+}
+
+// 2^x on the transcendental unit (exact 0 for -inf).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exchange a value with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// bf16 bit pattern of the low / high half of a 32-bit word, as float.
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Row index permutation used when loading the A operand of a score tile:
+// swapping bits 2 and 3 of the row index makes C-register r of lane half h
+// hold row 16 * (r / 8) + 8 * h + (r % 8), i.e. eight consecutive registers
+// cover eight consecutive rows, which is the k-slot order the next product
+// (scores times values) wants for its B operand.
+__device__ __forceinline__ int swap_bits23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// ---- staging of 4-row x 8-column bf16 blocks into LDS -----------------------
+// A block is rows r0..r0+3, columns 8g..8g+7 of a row-major [nrows][ld] bf16
+// matrix: four 16-byte vectors, one per row.  Rows >= nrows read as zero.
+__device__ __forceinline__ void load_block4x8(u32x4 (&blk)[4], const __bf16 *base, int r0, int nrows, int ld,
+                                              int g) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = r0 + u;
+    blk[u] = (r < nrows) ? ld16(base + (size_t)r * ld + 8 * g) : u32x4{0, 0, 0, 0};
+  }
+}
+
+// Row-major copy: lds[(lr0 + u) * stride + 8g .. +8) = row u of the block.
+__device__ __forceinline__ void store_block_rows(__bf16 *lds, int stride, int lr0, int g, const u32x4 (&blk)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) st16(lds + (lr0 + u) * stride + 8 * g, blk[u]);
+}
+
+// Transposed copy: ldsT[(8g + e) * strideT + lr0 .. +4) = column e of the block
+// (the four rows' values of column 8g+e), for e = 0..7.
+__device__ __forceinline__ void store_block_transposed(__bf16 *ldsT, int strideT, int lr0, int g,
+                                                       const u32x4 (&blk)[4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t a0 = blk[0][p], a1 = blk[1][p], a2 = blk[2][p], a3 = blk[3][p];
+    u32x2 lo, hi;
+    // v_perm_b32 picks bytes from {src0 (bytes 4..7), src1 (bytes 0..3)}
+    lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // col 2p of rows 0,1
+    lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);  // col 2p of rows 2,3
+    hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // col 2p+1 of rows 0,1
+    hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);  // col 2p+1 of rows 2,3
+    st8(ldsT + (8 * g + 2 * p) * strideT + lr0, lo);
+    st8(ldsT + (8 * g + 2 * p + 1) * strideT + lr0, hi);
+  }
+}
+
+}  // namespace fa

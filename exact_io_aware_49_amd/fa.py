@@ -1,0 +1,165 @@
+"""Thin ctypes binding of libfa.so (include/fa.h).
+
+The functions `fa_fwd`, `fa_bwd`, `fa_bwd_workspace_size`, `fa_status_string`
+and `fa_version` mirror the C ABI one to one: they take raw device pointers
+(ints), sizes and a stream handle, and return the status code.  `forward` and
+`backward` are the torch-facing conveniences: they check devices, dtypes and
+shapes, allocate outputs (and the backward workspace) with torch on the
+tensors' device, pass pointers and torch's current stream, and raise
+RuntimeError on any non-zero status.  All attention arithmetic happens in the
+HIP kernels; if libfa.so is missing or cannot load, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+STATUS_NAMES = {
+    0: "FA_OK",
+    1: "FA_ERR_NULL_POINTER",
+    2: "FA_ERR_BAD_SHAPE",
+    3: "FA_ERR_UNSUPPORTED_HEAD_DIM",
+    4: "FA_ERR_UNSUPPORTED_DTYPE",
+    5: "FA_ERR_BAD_SCALE",
+    6: "FA_ERR_MISALIGNED",
+    7: "FA_ERR_WORKSPACE_TOO_SMALL",
+    8: "FA_ERR_BAD_ARGUMENT",
+    9: "FA_ERR_HIP",
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libfa.so once; raise RuntimeError if it is missing or broken."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libfa.so not found at {path}; build it with `python -m exact_io_aware_49_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- raw C ABI mirror
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> int:
+    return load_library().fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream)
+
+
+def fa_bwd_workspace_size(B, H, N, d, dtype) -> int:
+    return load_library().fa_bwd_workspace_size(B, H, N, d, dtype)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, causal, scale, dtype,
+           stream) -> int:
+    return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                                 causal, scale, dtype, stream)
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(status).decode()
+
+
+def fa_version() -> int:
+    return load_library().fa_version()
+
+
+# ----------------------------------------------------------------- torch conveniences
+
+_DTYPES = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16}
+
+
+def _check(status: int):
+    if status != 0:
+        raise RuntimeError(fa_status_string(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise RuntimeError(f"unsupported dtype {t.dtype}; use torch.float32 or torch.bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _check_tensors(*ts):
+    ref = ts[0]
+    if not ref.is_cuda:
+        raise RuntimeError("tensors must be on a GPU device")
+    for t in ts:
+        if t.device != ref.device:
+            raise RuntimeError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise RuntimeError("tensors must be contiguous [B, H, N, d]")
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d), the scale of the attention equation."""
+    return float(d) ** -0.5
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Exact attention forward on the GPU.  q, k, v: [B, H, N, d] (bf16 or fp32).
+
+    Returns (o, lse): o like q, lse float32 [B, H, N].
+    """
+    load_library()
+    _check_tensors(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise RuntimeError("q, k, v must share shape [B, H, N, d] and dtype")
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensors(q, o, lse_t)
+    if o.shape != q.shape or o.dtype != q.dtype or lse_t.shape != (B, H, N) or lse_t.dtype != torch.float32:
+        raise RuntimeError("out / lse have the wrong shape or dtype")
+    _check(fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(), B, H, N, d,
+                  int(bool(causal)), scale, _dtype_code(q), _stream_handle(q.device)))
+    return o, lse_t
+
+
+def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, workspace=None):
+    """Exact attention backward with recomputation.  Returns (dq, dk, dv) like q."""
+    load_library()
+    _check_tensors(q, k, v, o, do, lse)
+    for t in (k, v, o, do):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise RuntimeError("q, k, v, o, do must share shape [B, H, N, d] and dtype")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise RuntimeError("lse must be float32 [B, H, N]")
+    scale = default_scale(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = fa_bwd_workspace_size(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                  B, H, N, d, int(bool(causal)), scale, code, _stream_handle(q.device)))
+    return dq, dk, dv

@@ -1,0 +1,126 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library libfa.so.
+ *
+ * The library computes exact attention, O = softmax(scale * Q K^T) V, the
+ * attention equation of "FlashAttention (DE)", section "Problematik der
+ * Standard-Attention", as one fused, tiled kernel that streams K/V blocks
+ * through on-chip memory and keeps a running row maximum and exponential sum
+ * (sections "Tiling und blockweise Verarbeitung", "Online-Softmax-Berechnung",
+ * "Zusammenfassen von Operationen in einem CUDA-Kernel").  The N x N score
+ * matrix is never written to device memory.  The forward also returns the
+ * per-row log-sum-exp; the backward keeps nothing else from the forward and
+ * recomputes the score blocks from it (Dutch glossary page "FlashAttention",
+ * section "Hoe werkt het?", bullet "Herberekening").
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller.  The library never
+ *    allocates device memory and keeps no pointer after a call returns.
+ *  - Tensors are contiguous row-major [B, H, N, d] (q, k, v, o, dout, dq, dk,
+ *    dv) and [B, H, N] (lse).  The element type of q, k, v, o, dout, dq, dk,
+ *    dv is `dtype`; lse is always float32.  Indexing is 64-bit.
+ *  - Every tensor pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work; completion is observed by synchronising that
+ *    stream.  Inputs are read-only; outputs are fully overwritten.  Outputs
+ *    that overlap inputs or each other are undefined behaviour.
+ *  - All arguments are validated before any HIP call.  On a validation error
+ *    the status is returned and nothing is enqueued.  A failed launch maps to
+ *    FA_ERR_HIP.  Nothing is printed; no exception crosses the ABI; the
+ *    library holds no mutable global state, so calls are thread-safe.
+ *  - causal = 1 applies the causal mask: query i sees key j iff j <= i
+ *    (positions counted from 0; queries and keys have the same length N).
+ *    Masked scores get probability exactly 0.
+ *  - scale must be finite and > 0 (the pages' value is 1/sqrt(d)).
+ *  - Supported: d in {64, 128}; B, H, N >= 1; B*H*N*d < 2^62.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#if defined(__GNUC__)
+#define FA_API __attribute__((visibility("default")))
+#else
+#define FA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_DTYPE_F32 = 0,  /* IEEE float32 inputs and outputs */
+  FA_DTYPE_BF16 = 1  /* bfloat16 inputs and outputs, float32 accumulation */
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_POINTER = 1,         /* a required pointer is NULL */
+  FA_ERR_BAD_SHAPE = 2,            /* B, H or N < 1, or the element count overflows */
+  FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128} */
+  FA_ERR_UNSUPPORTED_DTYPE = 4,    /* dtype unknown, or not supported by this entry point */
+  FA_ERR_BAD_SCALE = 5,            /* scale not finite or not > 0 */
+  FA_ERR_MISALIGNED = 6,           /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE_TOO_SMALL = 7,  /* workspace NULL or smaller than fa_bwd_workspace_size() */
+  FA_ERR_BAD_ARGUMENT = 8,         /* causal not 0 or 1 */
+  FA_ERR_HIP = 9                   /* a HIP launch or runtime call failed */
+} fa_status_t;
+
+/*
+ * Forward: o = softmax(scale * q k^T [causal mask]) v and, per query row,
+ * lse = ln sum_j exp(scale * q_i . k_j) over the visible keys (natural log,
+ * float32).  The lse is the normalisation value that fa_bwd consumes.
+ *
+ *   q, k, v : [B,H,N,d] inputs of `dtype`.
+ *   o       : [B,H,N,d] output of `dtype`.
+ *   lse     : [B,H,N] float32 output.
+ * dtype FA_DTYPE_BF16 runs both products on bf16 matrix cores with float32
+ * accumulation (P is rounded to bf16, nearest-even, before multiplying V);
+ * FA_DTYPE_F32 computes in float32 throughout.  No workspace: the forward
+ * uses no device memory beyond its arguments.
+ */
+FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int N, int d, int causal, float scale, int dtype,
+           void *stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes: the per-row
+ * D_i = sum_c dO_ic O_ic as float32 [B,H,N], rounded up to 256 bytes.
+ * Returns 0 for arguments fa_bwd would reject.
+ */
+FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward with recomputation.  Given the forward's inputs, its output o and
+ * its lse, and the upstream gradient dout = dL/dO, writes dq, dk, dv.  The
+ * score and probability blocks are recomputed from q, k and lse; nothing of
+ * size N x N is stored.
+ *
+ *   q, k, v, o, dout : [B,H,N,d] inputs of `dtype`.
+ *   lse              : [B,H,N] float32 from fa_fwd on the same q, k, v.
+ *   dq, dk, dv       : [B,H,N,d] outputs of `dtype`.
+ *   workspace        : device memory of at least fa_bwd_workspace_size()
+ *                      bytes, 16-byte aligned; contents on entry are ignored
+ *                      and are garbage on exit.
+ * Only FA_DTYPE_BF16 is supported (FA_ERR_UNSUPPORTED_DTYPE otherwise).
+ * Two kernels run on `stream`: one owns a block of queries and produces dq
+ * (and D), the other owns a block of keys and produces dk and dv.  No
+ * atomics are used, so dq, dk and dv are bitwise reproducible.
+ */
+FA_API int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const void *dout, const float *lse, void *dq, void *dk, void *dv,
+           void *workspace, size_t workspace_bytes,
+           int B, int H, int N, int d, int causal, float scale, int dtype,
+           void *stream);
+
+/* A static, human-readable string for a status code (never NULL). */
+FA_API const char *fa_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+FA_API int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

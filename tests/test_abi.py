@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented status codes before any HIP call.
+
+Fake, never-dereferenced pointer values are passed: validation returns first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_49_amd as fa
+from exact_io_aware_49_amd import fa as fab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+P = 0x10000  # aligned fake device pointers (never touched: validation fails first)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"FA_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    names = declared_symbols()
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    raw = ctypes.CDLL(fa.LIB_PATH)
+    for n in names:
+        getattr(raw, n)
+
+
+def test_status_strings_and_version():
+    for code, name in fab.STATUS_NAMES.items():
+        assert fa.fa_status_string(code).startswith(name)
+    assert "unknown" in fa.fa_status_string(12345)
+    assert fa.fa_version() == 10000
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=128, d=64, causal=0, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["causal"],
+                     a["scale"], a["dtype"], a["stream"])
+
+
+def bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, wsb=1 << 20, B=1, H=2, N=128, d=64,
+             causal=1, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                     a["wsb"], a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(B=1 << 30, H=1 << 30), 2),
+    (dict(d=32), 3), (dict(d=96), 3), (dict(d=256), 3),
+    (dict(dtype=2), 4), (dict(dtype=-1), 4),
+    (dict(scale=0.0), 5), (dict(scale=-0.125), 5), (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5),
+    (dict(q=P + 8), 6), (dict(o=P + 2), 6), (dict(lse=P + 4), 6),
+    (dict(causal=2), 8), (dict(causal=-1), 8),
+])
+def test_fwd_validation(kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), 1), (dict(dq=None), 1), (dict(lse=None), 1),
+    (dict(N=0), 2), (dict(d=80), 3), (dict(dtype=0), 4), (dict(scale=0.0), 5),
+    (dict(ws=None), 7), (dict(wsb=100), 7), (dict(dk=P + 8), 6), (dict(ws=P + 8), 6), (dict(causal=3), 8),
+])
+def test_bwd_validation(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_workspace_size():
+    assert fa.fa_bwd_workspace_size(4, 16, 2048, 64, 1) == 4 * 16 * 2048 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 1) == 256
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 0) == 0   # fp32 backward unsupported
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 96, 1) == 0
+    assert fa.fa_bwd_workspace_size(0, 1, 3, 64, 1) == 0
+
+
+def test_torch_api_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(RuntimeError):
+        fa.forward(q, q, q)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(fab, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        fab.load_library(str(tmp_path / "nope.so"))

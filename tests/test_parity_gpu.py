@@ -1,0 +1,215 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the float64 oracle.
+
+Every case draws seeded inputs, runs the GPU path, and compares against the
+oracle on the same (bf16-rounded) values.  The five named workloads run at their
+full sizes; where the oracle cannot evaluate every output in seconds it checks
+whole heads for a subset and sampled rows (each an exact oracle evaluation of
+that row) everywhere else.  Small sweeps cover ragged lengths, N = 1, both head
+dims, both masks and both dtypes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_49_amd import inputs
+import exact_io_aware_49_amd as fa
+from gpu_common import assert_close, dev, f32, host, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(q, k, v, causal, scale, dtype):
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+def check_fwd_full(q, k, v, causal, scale, dtype, tag, stress=False):
+    say(f"[fwd] {tag} shape={q.shape} causal={causal} dtype={dtype}")
+    o, lse = run_fwd(q, k, v, causal, scale, dtype)
+    ro, rl = oracle.attention_forward(q, k, v, causal, f32(scale))
+    eo = assert_close(f"{tag} O", o, ro, dtype, magnitude_scaled=stress)
+    el = assert_close(f"{tag} lse", lse, rl, dtype, lse=True, magnitude_scaled=stress)
+    say(f"   O max/rel {eo[0]:.2e}/{eo[1]:.2e}  lse max {el[0]:.2e}")
+
+
+# ------------------------------------------------------------------ named workloads
+
+def test_workload_fwd_f32_small():
+    need_gpu()
+    w = inputs.WORKLOADS["fwd_f32_b1h2n128d64"]
+    q, k, v = inputs.workload_inputs(w)
+    check_fwd_full(q, k, v, w.causal, w.scale, w.dtype, w.name)
+
+
+def test_workload_fwd_gpt2_causal():
+    need_gpu()
+    w = inputs.WORKLOADS["fwd_gpt2_causal_b8h12n1024d64"]
+    q, k, v = inputs.workload_inputs(w)
+    check_fwd_full(q, k, v, w.causal, w.scale, w.dtype, w.name)
+
+
+def _sampled_rows(N, rng, n_rand):
+    rows = set(range(0, 4)) | set(range(N - 4, N)) | set(range(127, 130))
+    rows |= set(int(x) for x in rng.integers(0, N, n_rand))
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+def check_fwd_sampled(w, full_heads, n_rand):
+    need_gpu()
+    q, k, v = inputs.workload_inputs(w)
+    say(f"[fwd] {w.name} (full heads {full_heads}, sampled rows elsewhere)")
+    o, lse = run_fwd(q, k, v, w.causal, w.scale, w.dtype)
+    s = f32(w.scale)
+    rng = np.random.Generator(np.random.PCG64(1000 + w.seed))
+    B, H, N, d = w.shape
+    worst = [0.0, 0.0]
+    for b in range(B):
+        for h in range(H):
+            if (b, h) in full_heads:
+                ro, rl = oracle.attention_forward(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1],
+                                                  v[b:b + 1, h:h + 1], w.causal, s)
+                e = assert_close(f"{w.name} O[{b},{h}]", o[b, h], ro[0, 0], w.dtype)
+                assert_close(f"{w.name} lse[{b},{h}]", lse[b, h], rl[0, 0], w.dtype, lse=True)
+            else:
+                rows = _sampled_rows(N, rng, n_rand)
+                ro, rl = oracle.attention_forward_rows(q, k, v, w.causal, s, b, h, rows)
+                e = assert_close(f"{w.name} O[{b},{h}] rows", o[b, h, rows], ro, w.dtype)
+                assert_close(f"{w.name} lse[{b},{h}] rows", lse[b, h, rows], rl, w.dtype, lse=True)
+            worst = [max(worst[0], e[0]), max(worst[1], e[1])]
+    say(f"   worst O max/rel {worst[0]:.2e}/{worst[1]:.2e}")
+
+
+def test_workload_fwd_encoder():
+    check_fwd_sampled(inputs.WORKLOADS["fwd_encoder_b4h16n4096d128"], {(0, 0), (1, 7), (3, 15)}, 48)
+
+
+def test_workload_fwd_longctx_causal():
+    check_fwd_sampled(inputs.WORKLOADS["fwd_longctx_causal_b1h32n32768d128"], set(), 8)
+
+
+def run_bwd(q, k, v, do, causal, scale, dtype="bf16"):
+    qd, kd, vd, dod = (dev(x, dtype) for x in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv)
+
+
+def check_bwd_heads(q, k, v, do, causal, scale, heads, tag, stress=False):
+    say(f"[bwd] {tag} shape={q.shape} causal={causal} heads checked={len(heads)}")
+    dq, dk, dv = run_bwd(q, k, v, do, causal, scale)
+    s = f32(scale)
+    worst = {}
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], causal, s)
+        for name, got, ref in (("dQ", dq[b, h], rq[0, 0]), ("dK", dk[b, h], rk[0, 0]), ("dV", dv[b, h], rv[0, 0])):
+            e = assert_close(f"{tag} {name}[{b},{h}]", got, ref, "bf16", magnitude_scaled=stress)
+            worst[name] = max(worst.get(name, (0, 0)), e)
+    say("   worst " + "  ".join(f"{n} max/rel {e[0]:.2e}/{e[1]:.2e}" for n, e in worst.items()))
+    return dq, dk, dv
+
+
+def test_workload_bwd_causal():
+    need_gpu()
+    w = inputs.WORKLOADS["bwd_causal_b4h16n2048d64"]
+    q, k, v, do = inputs.workload_inputs(w)
+    heads = [(0, 0), (0, 15), (1, 3), (2, 8), (3, 0), (3, 15)]
+    dq, dk, dv = check_bwd_heads(q, k, v, do, w.causal, w.scale, heads, w.name)
+    # every head: gradient identities of the exact result (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i)
+    assert np.abs(dk.sum(axis=2)).max() < 0.5
+    assert np.abs(dv.sum(axis=2) - do.astype(np.float64).sum(axis=2)).max() < 0.5
+
+
+def test_bwd_encoder_shape():
+    """The backward at the non-causal d=128 encoder shape (the benchmark's step)."""
+    need_gpu()
+    w = inputs.WORKLOADS["fwd_encoder_b4h16n4096d128"]
+    q, k, v, do = inputs.gen_qkv(w.shape, "bf16", w.seed, with_do=True)
+    check_bwd_heads(q, k, v, do, False, w.scale, [(0, 0), (3, 15)], "bwd_encoder_b4h16n4096d128")
+
+
+# ------------------------------------------------------------------ small sweeps
+
+SWEEP_N = [1, 17, 64, 100, 128, 129, 255, 300]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_sweep(dtype, d, causal):
+    need_gpu()
+    for i, N in enumerate(SWEEP_N):
+        B, H = (1 + i % 2, 1 + (i % 3))
+        q, k, v = inputs.gen_qkv((B, H, N, d), dtype, 500 + 7 * i + d)
+        check_fwd_full(q, k, v, causal, d ** -0.5, dtype, f"sweep N={N}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_sweep(d, causal):
+    need_gpu()
+    for i, N in enumerate([1, 17, 64, 129, 200, 384]):
+        B, H = 1, 1 + i % 2
+        q, k, v, do = inputs.gen_qkv((B, H, N, d), "bf16", 900 + 3 * i + d, with_do=True)
+        check_bwd_heads(q, k, v, do, causal, d ** -0.5, [(0, h) for h in range(H)], f"sweep N={N}")
+
+
+# ------------------------------------------------------------------ stress / structure
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores_force_rescale(causal):
+    """Scores that rise along the keys make the running maximum move on every tile."""
+    need_gpu()
+    N, d = 1024, 64
+    q, k, v = inputs.gen_qkv((1, 2, N, d), "bf16", 77)
+    ramp = np.linspace(0.0, 6.0, N, dtype=np.float32)
+    q[..., 0] = 4.0
+    k[..., 0] = inputs.bf16_round(ramp)[None, None, :]
+    q, k = inputs.bf16_round(q), inputs.bf16_round(k)
+    check_fwd_full(q, k, v, causal, 1.0, "bf16", "growing scores", stress=True)
+    do = inputs.gen_qkv((1, 2, N, d), "bf16", 78)[0]
+    check_bwd_heads(q, k, v, do, causal, 1.0, [(0, 0), (0, 1)], "growing scores", stress=True)
+
+
+def test_peaky_scale():
+    need_gpu()
+    q, k, v = inputs.gen_qkv((2, 2, 512, 128), "bf16", 79)
+    check_fwd_full(q, k, v, True, 4 * 128 ** -0.5, "bf16", "peaky x4", stress=True)
+
+
+def test_causal_row0_is_v0_exactly():
+    need_gpu()
+    q, k, v = inputs.gen_qkv((2, 3, 256, 64), "bf16", 80)
+    o, _ = run_fwd(q, k, v, True, 0.125, "bf16")
+    assert np.array_equal(o[:, :, 0], v[:, :, 0].astype(np.float64))
+
+
+def test_forward_and_backward_are_deterministic():
+    need_gpu()
+    q, k, v, do = (dev(x, "bf16") for x in inputs.gen_qkv((2, 4, 777, 64), "bf16", 81, with_do=True))
+    o1, l1 = fa.forward(q, k, v, causal=True)
+    o2, l2 = fa.forward(q, k, v, causal=True)
+    g1 = fa.backward(q, k, v, o1, do, l1, causal=True)
+    g2 = fa.backward(q, k, v, o1, do, l1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_golden_rational_case_fp32():
+    """The hand-derived closed form of tests/golden, run through the fp32 GPU path (d padded to 64)."""
+    need_gpu()
+    import pins
+    scale, q2, k2, v2, do2, cases = pins.load_rational_case()
+    pad = lambda a: np.pad(a, ((0, 0), (0, 62)))[None, None].astype(np.float32)  # noqa: E731
+    for key, causal in (("noncausal", False), ("causal", True)):
+        o, lse = run_fwd(pad(q2), pad(k2), pad(v2), causal, scale, "f32")
+        assert np.abs(o[0, 0, :, :2] - cases[key]["O"]).max() <= 1e-5
+        assert np.abs(o[0, 0, :, 2:]).max() == 0.0
+        assert np.abs(lse[0, 0] - cases[key]["lse"]).max() <= 1e-5
