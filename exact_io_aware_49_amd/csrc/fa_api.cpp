@@ -27,6 +27,9 @@ int check_common(int B, int H, int N, int d, int causal, float scale, int dtype)
   const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
   if (bh > (1ull << 55) / (unsigned long long)N) return FA_ERR_BAD_SHAPE;
   if (bh * (((unsigned long long)N + 63) / 64) > 0x7fffffffull) return FA_ERR_BAD_SHAPE;
+  // one head's [N, d] slab is addressed through 32-bit buffer offsets
+  const unsigned long long esize = (dtype == FA_DTYPE_F32) ? 4ull : 2ull;
+  if ((unsigned long long)N * (unsigned long long)d * esize >= (1ull << 31)) return FA_ERR_BAD_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_BAD_ARGUMENT;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_SCALE;
   return FA_OK;

@@ -86,7 +86,7 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
       }
     }
   }
-  const float drow = dpart + swap_halves(dpart);
+  const float drow = sum_with_partner(dpart);
   const float lse2 = q_ok ? LSE[(size_t)bh * N + my_q] * kLog2e : 0.f;
   if (q_ok && half == 0) Dsum[(size_t)bh * N + my_q] = drow;
 

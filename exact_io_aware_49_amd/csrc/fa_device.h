@@ -22,6 +22,11 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -38,11 +43,29 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 __device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
 
-// Pack two floats into bf16 (round to nearest, ties to even), low half first.
+// Pack two floats into bf16 (round to nearest, ties to even), low half first:
+// one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const floatx2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// lo + hi of a packed bf16 pair, accumulated in float32 (v_dot2c_f32_bf16 with (1, 1)).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
+
+// Both halves of the wave exchange a value: returns {lanes 0..31 of x twice,
+// lanes 32..63 of x twice} as (first, second); per lane, one of the two is its
+// own value and the other its partner's (lane ^ 32).  v_permlane32_swap_b32.
+__device__ __forceinline__ float max_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Eight floats -> bf16x8 operand.
@@ -109,6 +132,51 @@ __device__ __forceinline__ void store_block_transposed(__bf16 *ldsT, int strideT
     st8(ldsT + (8 * g + 2 * p) * strideT + lr0, lo);
     st8(ldsT + (8 * g + 2 * p + 1) * strideT + lr0, hi);
   }
+}
+
+// ---- direct global -> LDS loads ------------------------------------------
+// A buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes
+// return zero, which is how rows past the end of a sequence read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from rsrc + voffset into LDS at lds_wave_base + 16 * lane
+// (buffer_load_dwordx4 ... lds).  lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, void *lds_wave_base, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, FA_LDS(void, lds_wave_base), 16, (int)voffset, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)FA_LDS(const void, p);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j supplies the address
+// of 4 consecutive bf16 of some row; lane i receives element (i % 4) of the
+// rows supplied by lanes 4t + i / 4, t = 0..3 (in that order).  Used to read a
+// transposed operand straight from a row-major LDS tile.
+//
+// Issued through inline asm: the compiler would otherwise wait for every
+// outstanding global->LDS transfer before it (it cannot prove the transfer
+// writes a different buffer).  The caller must therefore (1) only read LDS
+// whose transfers are known complete (vmcnt(0) + barrier) and (2) call
+// lds_wait() on the results before using them.
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+
+// s_waitcnt lgkmcnt(0), with the given registers routed through it so that
+// no use of them can be scheduled before the wait.
+__device__ __forceinline__ void lds_wait(u32x2 &a, u32x2 &b, u32x2 &c, u32x2 &d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void lds_wait(u32x2 &a, u32x2 &b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
 }
 
 }  // namespace fa

@@ -12,22 +12,23 @@
 // Mapping to one workgroup (4 waves, 256 threads), BR = 128 query rows:
 //   * Each wave owns 32 query rows.  Its Q rows sit in VGPRs as the B operand
 //     of S^T = K Q^T (lane = query row, 8 consecutive head-dim slots per lane).
-//   * A K/V tile of BC keys (BC = 64 for d = 128, 128 for d = 64) is staged per
-//     iteration: K row-major in LDS (padded rows), V transposed in LDS so that
-//     the values of one head-dim column for consecutive keys are contiguous.
-//     Staging is double-buffered: the global loads of tile j+1 are issued before
-//     tile j is computed and land in LDS after it.
-//   * S^T tiles (32 keys x 32 queries) are computed with v_mfma_f32_32x32x16_bf16.
-//     The result leaves each lane holding one query row and 16 of its keys per
-//     tile; the other 16 sit in the lane 32 away.  The row maximum therefore
-//     needs one cross-half exchange per tile.
-//   * P = 2^(S c - m c) with c = scale * log2(e) (one FMA + one v_exp_f32 per
-//     score), rounded to bf16, is directly the B operand of O^T += V^T P^T, so P
-//     never touches LDS.  O^T accumulates in registers: lane = query row.
-//   * The running maximum is only moved when the tile maximum exceeds it by more
-//     than 2^8 in exp2 units.  Both O and the exponential sum are expressed
-//     relative to the same reference, so the final O / l is unchanged; values
-//     stay below 2^8 times the row sum, far from float32 overflow.
+//   * A K/V tile of BC keys (BC = 64 for d = 128, 128 for d = 64) goes from HBM
+//     straight into LDS with buffer_load ... lds (no staging registers), double
+//     buffered: tile j+1 is in flight while tile j is computed.  Rows past the
+//     end of the sequence come back as zero from the buffer descriptor's range
+//     check.  Tiles are row-major with the 16-byte chunks of each row XOR-
+//     permuted by a function of the row, so the score reads (16 rows, one chunk)
+//     and the transposed value reads (4 rows, 4 chunks) hit distinct banks.
+//   * S^T tiles (32 keys x 32 queries) use v_mfma_f32_32x32x16_bf16; each lane
+//     ends up with one query row and 16 of its keys per tile, the other 16 in
+//     the lane 32 away, so the row maximum needs one v_permlane32_swap.
+//   * P = 2^(S c - m c), c = scale * log2(e), is rounded to bf16 and used as the
+//     B operand of O^T += V^T P^T directly from registers.  The V^T operand is
+//     read from the row-major V tile with ds_read_b64_tr_b16.  The row sum adds
+//     the same bf16 P values the product uses (v_dot2c_f32_bf16).
+//   * The running maximum only moves when a tile's maximum exceeds it by more
+//     than 2^8 in exp2 units; O and l share the reference, so O / l is
+//     unchanged and every P stays below 2^8.
 //   * Causal: tiles entirely above the diagonal are never loaded; a wave whose
 //     rows are all above a tile skips its math; only diagonal and ragged tiles
 //     pay for masking.
@@ -39,18 +40,28 @@ namespace {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BR = 128;                  // query rows per workgroup
-  static constexpr int BC = (D == 128) ? 64 : 128; // keys per tile
-  static constexpr int NKT = BC / 32;             // 32-key score tiles per K/V tile
-  static constexpr int KSTEPS = D / 16;           // MFMA k-steps over the head dim
-  static constexpr int CT = D / 32;               // 32-column output tiles
-  static constexpr int KSTRIDE = D + 8;           // bf16 elements per K row in LDS
-  static constexpr int VSTRIDE = BC + 8;          // bf16 elements per V^T row in LDS
-  static constexpr int KTILE = BC * KSTRIDE;      // bf16 elements per K buffer
-  static constexpr int VTILE = D * VSTRIDE;       // bf16 elements per V^T buffer
-  static constexpr int KVEC = BC * D / 8 / 256;   // 16-byte K vectors per thread per tile (= 4)
-  static constexpr int KQUADS = BC / 4;           // 4-key groups for the V transpose
+  static constexpr int BR = 128;                    // query rows per workgroup
+  static constexpr int BC = (D == 128) ? 64 : 128;  // keys per tile
+  static constexpr int NKT = BC / 32;               // 32-key score tiles per K/V tile
+  static constexpr int KSTEPS = D / 16;             // MFMA k-steps over the head dim
+  static constexpr int CT = D / 32;                 // 32-column output tiles
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int RPI = 1024 / ROW_BYTES;      // rows per wave-wide 16-byte load
+  static constexpr int TILE_BYTES = BC * ROW_BYTES;
+  static constexpr int LPW = TILE_BYTES / 1024 / 4; // loads per wave per tensor per tile
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 };
+
+// Chunk permutations (physical chunk = logical chunk ^ swz(row)).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return (D == 128) ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 // Map the linear workgroup id to (batch*head, query block).  Workgroups are
 // dispatched round-robin over the 8 XCDs; grouping consecutive ids of one XCD
@@ -64,11 +75,9 @@ __device__ __forceinline__ void map_block(int bid, int nqb, int nbh, bool causal
     id = (bid & 7) * per_xcd + (bid >> 3);
   }
   if (causal) {
-    // within each XCD's contiguous range, order by descending query block
     const int per_xcd = ((total & 7) == 0) ? (total >> 3) : total;
     const int base = (id / per_xcd) * per_xcd;
     const int local = id - base;
-    // heads covered by this range (per_xcd is a multiple of nqb when nbh % 8 == 0)
     if (per_xcd % nqb == 0) {
       const int heads_here = per_xcd / nqb;
       const int qrank = local / heads_here;
@@ -88,9 +97,9 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE,
-                   int N, int nbh, float scale_log2e, float scale) {
+                   int N, int nbh, float scale_log2e) {
   using C = FwdCfg<D>;
-  __shared__ __align__(16) __bf16 smem[2 * (C::KTILE + C::VTILE)];
+  __shared__ __align__(1024) unsigned char smem[2 * C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,113 +112,86 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   map_block(blockIdx.x, nqb, nbh, CAUSAL, bh, qb);
 
   const size_t head_off = (size_t)bh * (size_t)N * D;
-  const __bf16 *Qh = Q + head_off;
-  const __bf16 *Kh = K + head_off;
-  const __bf16 *Vh = V + head_off;
+  const uint32_t head_bytes = (uint32_t)N * C::ROW_BYTES;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + head_off, head_bytes);
 
-  const int q0 = qb * C::BR;              // first query row of the workgroup
-  const int qw0 = q0 + wave * 32;         // first query row of this wave
-  const int my_q = qw0 + l32;             // this lane's query row
+  const int q0 = qb * C::BR;       // first query row of the workgroup
+  const int qw0 = q0 + wave * 32;  // first query row of this wave
+  const int my_q = qw0 + l32;      // this lane's query row
 
   // ---- Q fragments: B operand, lane = query row, slots = d in [16*ks + 8*half, +8)
   bf16x8 qf[C::KSTEPS];
   {
     const bool ok = my_q < N;
-    const __bf16 *qrow = Qh + (size_t)(ok ? my_q : 0) * D + 8 * half;
+    const __bf16 *qrow = Q + head_off + (size_t)(ok ? my_q : 0) * D + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      u32x4 v = ok ? ld16(qrow + 16 * ks) : u32x4{0, 0, 0, 0};
-      qf[ks] = as_bf16x8(v);
-    }
+    for (int ks = 0; ks < C::KSTEPS; ++ks) qf[ks] = as_bf16x8(ok ? ld16(qrow + 16 * ks) : u32x4{0, 0, 0, 0});
   }
 
   // ---- number of key tiles this workgroup visits
   const int ntiles_all = (N + C::BC - 1) / C::BC;
   int ntiles = ntiles_all;
-  if (CAUSAL) {
-    const int last_q = min(q0 + C::BR, N) - 1;
-    ntiles = min(ntiles_all, last_q / C::BC + 1);
-  }
+  if (CAUSAL) ntiles = min(ntiles_all, (min(q0 + C::BR, N) - 1) / C::BC + 1);
 
-  // ---- staging helpers: thread t owns KVEC K vectors and one 4x8 V block per tile
-  const int k_g = tid % (D / 8);          // 16-byte column group of K
-  const int k_r = tid / (D / 8);          // first K row; rows k_r + (256/(D/8))*u
-  constexpr int K_ROWSTEP = 256 / (D / 8);
-  const int v_kq = tid % C::KQUADS;       // key quad of V
-  const int v_g = tid / C::KQUADS;        // 8-wide head-dim group of V
-
-  u32x4 kreg[C::KVEC];
-  u32x4 vreg[4];
-
-  auto load_tile = [&](int t) {
-    const int kb = t * C::BC;
+  // ---- direct loads: wave w fills rows [(w*LPW + u)*RPI, +RPI) of K and V
+  const int ld_row_in = lane / C::CPR;  // row within one load
+  const int ld_chunk = lane % C::CPR;   // physical chunk this lane fills
+  auto issue_tile = [&](int t, int buf) {
+    unsigned char *kbase = smem + buf * C::STAGE_BYTES;
+    unsigned char *vbase = kbase + C::TILE_BYTES;
 #pragma unroll
-    for (int u = 0; u < C::KVEC; ++u) {
-      const int r = kb + k_r + K_ROWSTEP * u;
-      kreg[u] = (r < N) ? ld16(Kh + (size_t)r * D + 8 * k_g) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = kb + 4 * v_kq + u;
-      vreg[u] = (r < N) ? ld16(Vh + (size_t)r * D + 8 * v_g) : u32x4{0, 0, 0, 0};
+    for (int u = 0; u < C::LPW; ++u) {
+      const int row0 = (wave * C::LPW + u) * C::RPI;
+      const int row = row0 + ld_row_in;
+      const uint32_t grow = (uint32_t)(t * C::BC + row) * C::ROW_BYTES;
+      load_lds16(krs, kbase + row0 * C::ROW_BYTES, grow + 16u * (ld_chunk ^ swz_k<D>(row)));
+      load_lds16(vrs, vbase + row0 * C::ROW_BYTES, grow + 16u * (ld_chunk ^ swz_v<D>(row)));
     }
   };
 
-  auto store_tile = [&](int buf) {
-    __bf16 *Ks = smem + buf * (C::KTILE + C::VTILE);
-    __bf16 *Vt = Ks + C::KTILE;
-#pragma unroll
-    for (int u = 0; u < C::KVEC; ++u) st16(Ks + (k_r + K_ROWSTEP * u) * C::KSTRIDE + 8 * k_g, kreg[u]);
-    // 4 keys x 8 columns -> 8 rows of V^T, 4 keys each (8 bytes)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      // column 2p (low halves) and 2p+1 (high halves) of the four key rows
-      const uint32_t a0 = vreg[0][p], a1 = vreg[1][p], a2 = vreg[2][p], a3 = vreg[3][p];
-      u32x2 lo, hi;
-      lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-      st8(Vt + (8 * v_g + 2 * p) * C::VSTRIDE + 4 * v_kq, lo);
-      st8(Vt + (8 * v_g + 2 * p + 1) * C::VSTRIDE + 4 * v_kq, hi);
-    }
-  };
+  // ---- per-lane read offsets
+  // score A operand: K row 32*kt + swap_bits23(l32), logical chunk 2*ks + half
+  const int krow = swap_bits23(l32);
+  // value A operand (transposed read): lane j = l & 15 of its group addresses
+  // row key0 + (j >> 2), column cbase + 4 * (j & 3); cbase = 32*ct + 16*((l >> 4) & 1)
+  const int tr_t = (lane & 15) >> 2;
+  const int tr_q = lane & 3;
+  const int tr_cb = 16 * ((lane >> 4) & 1);
 
   floatx16 oacc[C::CT];
 #pragma unroll
   for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = floatx16{0};
-  float m_ref = -INFINITY;  // running maximum of raw scores (q.k, unscaled)
+  float m_ref = -INFINITY;  // running reference maximum of raw scores q.k
   float l_part = 0.f;       // this lane's part of the running exponential sum
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  // A-operand row for the score tile: K row swap_bits23(l32) of each 32-key tile
-  const int krow_perm = swap_bits23(l32);
+  issue_tile(0, 0);
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    const bool prefetch = (t + 1) < ntiles;
-    if (prefetch) load_tile(t + 1);
+    wait_vmem();
+    __syncthreads();  // tile t is in LDS for everyone; tile t-1 is no longer read
+    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
 
     const int kb = t * C::BC;
     const bool wave_active = !CAUSAL || (kb <= qw0 + 31);
     if (wave_active) {
-      const __bf16 *Ks = smem + buf * (C::KTILE + C::VTILE);
-      const __bf16 *Vt = Ks + C::KTILE;
+      const unsigned char *Ks = smem + buf * C::STAGE_BYTES;
+      const uint32_t vbase_addr = lds_addr(Ks + C::TILE_BYTES);
 
       // ---- S^T = K Q^T for NKT tiles of 32 keys
       floatx16 s[C::NKT];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt) {
-        s[kt] = floatx16{0};
-        const __bf16 *krow = Ks + (32 * kt + krow_perm) * C::KSTRIDE + 8 * half;
+        const int r = 32 * kt + krow;
+        const unsigned char *rowp = Ks + r * C::ROW_BYTES;
+        const int sw = swz_k<D>(r);
+        bf16x8 a[C::KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) {
-          bf16x8 a = as_bf16x8(ld16(krow + 16 * ks));
-          s[kt] = mfma32x32x16(a, qf[ks], s[kt]);
-        }
+        for (int ks = 0; ks < C::KSTEPS; ++ks) a[ks] = as_bf16x8(ld16(rowp + 16 * ((2 * ks + half) ^ sw)));
+        s[kt] = floatx16{0};
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) s[kt] = mfma32x32x16(a[ks], qf[ks], s[kt]);
       }
 
       // ---- masking (diagonal and ragged tiles only)
@@ -226,13 +208,16 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         }
       }
 
-      // ---- row maximum of this tile (lane holds 16*NKT keys, partner lane the rest)
+      // ---- row maximum of this tile
       float mloc = s[0][0];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kt][r]);
-      const float m_tile = fmaxf(mloc, swap_halves(mloc));
+        for (int r = (kt == 0 ? 1 : 0); r < 16; r += 2) {
+          if (r + 1 < 16) mloc = fmaxf(mloc, fmaxf(s[kt][r], s[kt][r + 1]));
+          else mloc = fmaxf(mloc, s[kt][r]);
+        }
+      const float m_tile = max_with_partner(mloc);
       const float m_new = fmaxf(m_ref, m_tile);
 
       // ---- move the reference maximum only when the scores outgrow it by > 2^8
@@ -248,34 +233,46 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
       }
       const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * scale_log2e;
 
-      // ---- P = 2^(S c - m c), its row sum, and O^T += V^T P^T
+      // ---- P = 2^(S c - m c) in bf16, its row sum, and O^T += V^T P^T
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          float p[8];
+          u32x4 pw;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            p[i] = fast_exp2(__builtin_fmaf(s[kt][8 * m + i], scale_log2e, -mc));
-            l_part += p[i];
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[kt][8 * m + 2 * i], scale_log2e, -mc));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kt][8 * m + 2 * i + 1], scale_log2e, -mc));
+            pw[i] = pack_bf16x2(p0, p1);
+            l_part = add_bf16_pair(pw[i], l_part);
           }
-          const bf16x8 pb = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-          const int key_off = 32 * kt + 16 * m + 8 * half;
+          const bf16x8 pb = as_bf16x8(pw);
+          const int key0 = 32 * kt + 16 * m + 8 * half + tr_t;
+          const uint32_t a_lo = vbase_addr + key0 * C::ROW_BYTES + 8 * (tr_q & 1);
+          const uint32_t a_hi = a_lo + 4 * C::ROW_BYTES;
+          const int sw_lo = swz_v<D>(key0), sw_hi = swz_v<D>(key0 + 4);
 #pragma unroll
-          for (int ct = 0; ct < C::CT; ++ct) {
-            bf16x8 a = as_bf16x8(ld16(Vt + (32 * ct + l32) * C::VSTRIDE + key_off));
-            oacc[ct] = mfma32x32x16(a, pb, oacc[ct]);
+          for (int c2 = 0; c2 < C::CT; c2 += 2) {
+            // two 32-column tiles per batch: four transposed reads, one wait
+            const int ch0 = (32 * c2 + tr_cb) / 8 + (tr_q >> 1);
+            const int ch1 = ch0 + 4;
+            u32x2 l0 = ds_read_tr16(a_lo + 16 * (ch0 ^ sw_lo));
+            u32x2 h0 = ds_read_tr16(a_hi + 16 * (ch0 ^ sw_hi));
+            u32x2 l1 = ds_read_tr16(a_lo + 16 * (ch1 ^ sw_lo));
+            u32x2 h1 = ds_read_tr16(a_hi + 16 * (ch1 ^ sw_hi));
+            lds_wait(l0, h0, l1, h1);
+            const u32x4 a0 = {l0[0], l0[1], h0[0], h0[1]};
+            const u32x4 a1 = {l1[0], l1[1], h1[0], h1[1]};
+            oacc[c2] = mfma32x32x16(as_bf16x8(a0), pb, oacc[c2]);
+            oacc[c2 + 1] = mfma32x32x16(as_bf16x8(a1), pb, oacc[c2 + 1]);
           }
         }
       }
     }
-
-    if (prefetch) store_tile(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
-  const float l_tot = l_part + swap_halves(l_part);
+  const float l_tot = sum_with_partner(l_part);
   if (my_q < N) {
     const float inv = 1.f / l_tot;
     __bf16 *orow = O + head_off + (size_t)my_q * D;
@@ -289,11 +286,8 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         st8(orow + 32 * ct + 8 * g + 4 * half, w);
       }
     }
-    if (half == 0) {
-      LSE[(size_t)bh * N + my_q] = (m_ref * scale_log2e + __log2f(l_tot)) * kLn2;
-    }
+    if (half == 0) LSE[(size_t)bh * N + my_q] = (m_ref * scale_log2e + __log2f(l_tot)) * kLn2;
   }
-  (void)scale;
 }
 
 template <int D, bool CAUSAL>
@@ -306,7 +300,7 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, N, nbh,
-                     scale * kLog2e, scale);
+                     scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@
  *    (positions counted from 0; queries and keys have the same length N).
  *    Masked scores get probability exactly 0.
  *  - scale must be finite and > 0 (the pages' value is 1/sqrt(d)).
- *  - Supported: d in {64, 128}; B, H, N >= 1; B*H*N*d < 2^62.
+ *  - Supported: d in {64, 128}; B, H, N >= 1; B*H*N*d < 2^62; one head's
+ *    N*d elements below 2^31 bytes (N < 8,388,608 for bf16 at d = 128).
  */
 #ifndef FA_H_
 #define FA_H_

@@ -60,6 +60,7 @@ def bwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
     (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(B=1 << 30, H=1 << 30), 2),
+    (dict(N=1 << 24, d=64), 2), (dict(N=1 << 23, d=128, dtype=1), 2), (dict(N=(1 << 22) + 64, d=128, dtype=0), 2),
     (dict(d=32), 3), (dict(d=96), 3), (dict(d=256), 3),
     (dict(dtype=2), 4), (dict(dtype=-1), 4),
     (dict(scale=0.0), 5), (dict(scale=-0.125), 5), (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5),
