@@ -14,6 +14,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -27,6 +30,16 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 #define FA_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 (compile-time loop).
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -167,6 +180,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 __device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
   u32x2 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+
+// max(a, b, c) in one v_max3_f32 (no canonicalisation of the operands).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
 

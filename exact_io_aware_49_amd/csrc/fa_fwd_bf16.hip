@@ -12,10 +12,12 @@
 // Mapping to one workgroup (4 waves, 256 threads), BR = 128 query rows:
 //   * Each wave owns 32 query rows.  Its Q rows sit in VGPRs as the B operand
 //     of S^T = K Q^T (lane = query row, 8 consecutive head-dim slots per lane).
-//   * A K/V tile of BC keys (BC = 64 for d = 128, 128 for d = 64) goes from HBM
-//     straight into LDS with buffer_load ... lds (no staging registers), double
-//     buffered: tile j+1 is in flight while tile j is computed.  Rows past the
-//     end of the sequence come back as zero from the buffer descriptor's range
+//   * A K/V tile of BC = 64 keys goes from HBM
+//     straight into LDS with buffer_load ... lds (no staging registers).  K runs
+//     one tile ahead of V: while tile j's softmax and P V product run, the
+//     scores of tile j+1 are already being computed from LDS, and K(j+2) and
+//     V(j+1) are in flight (two K and two V buffers, 64 KB).  Rows past the end
+//     of the sequence come back as zero from the buffer descriptor's range
 //     check.  Tiles are row-major with the 16-byte chunks of each row XOR-
 //     permuted by a function of the row, so the score reads (16 rows, one chunk)
 //     and the transposed value reads (4 rows, 4 chunks) hit distinct banks.
@@ -41,7 +43,7 @@ namespace {
 template <int D>
 struct FwdCfg {
   static constexpr int BR = 128;                    // query rows per workgroup
-  static constexpr int BC = (D == 128) ? 64 : 128;  // keys per tile
+  static constexpr int BC = 64;                     // keys per tile
   static constexpr int NKT = BC / 32;               // 32-key score tiles per K/V tile
   static constexpr int KSTEPS = D / 16;             // MFMA k-steps over the head dim
   static constexpr int CT = D / 32;                 // 32-column output tiles
@@ -99,11 +101,14 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE,
                    int N, int nbh, float scale_log2e) {
   using C = FwdCfg<D>;
-  __shared__ __align__(1024) unsigned char smem[2 * C::STAGE_BYTES];
+  constexpr int TB = C::TILE_BYTES;
+  constexpr int RB = C::ROW_BYTES;
+  // LDS: K buffers at [0, TB) and [TB, 2TB), V buffers at [2TB, 3TB) and [3TB, 4TB)
+  __shared__ __align__(1024) unsigned char smem[4 * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -112,7 +117,7 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   map_block(blockIdx.x, nqb, nbh, CAUSAL, bh, qb);
 
   const size_t head_off = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * C::ROW_BYTES;
+  const uint32_t head_bytes = (uint32_t)N * RB;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + head_off, head_bytes);
 
@@ -134,30 +139,54 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   int ntiles = ntiles_all;
   if (CAUSAL) ntiles = min(ntiles_all, (min(q0 + C::BR, N) - 1) / C::BC + 1);
 
-  // ---- direct loads: wave w fills rows [(w*LPW + u)*RPI, +RPI) of K and V
-  const int ld_row_in = lane / C::CPR;  // row within one load
-  const int ld_chunk = lane % C::CPR;   // physical chunk this lane fills
-  auto issue_tile = [&](int t, int buf) {
-    unsigned char *kbase = smem + buf * C::STAGE_BYTES;
-    unsigned char *vbase = kbase + C::TILE_BYTES;
+  // ---- direct loads: wave w fills rows [(w*LPW + u)*RPI, +RPI) of a tile
+  const int ld_row_in = lane / C::CPR;
+  const int ld_chunk = lane % C::CPR;
+  auto issue_k = [&](int t, int lds_off) {
 #pragma unroll
     for (int u = 0; u < C::LPW; ++u) {
       const int row0 = (wave * C::LPW + u) * C::RPI;
       const int row = row0 + ld_row_in;
-      const uint32_t grow = (uint32_t)(t * C::BC + row) * C::ROW_BYTES;
-      load_lds16(krs, kbase + row0 * C::ROW_BYTES, grow + 16u * (ld_chunk ^ swz_k<D>(row)));
-      load_lds16(vrs, vbase + row0 * C::ROW_BYTES, grow + 16u * (ld_chunk ^ swz_v<D>(row)));
+      const uint32_t g = (uint32_t)(t * C::BC + row) * RB + 16u * (ld_chunk ^ swz_k<D>(row));
+      load_lds16(krs, smem + lds_off + row0 * RB, g);
+    }
+  };
+  auto issue_v = [&](int t, int lds_off) {
+#pragma unroll
+    for (int u = 0; u < C::LPW; ++u) {
+      const int row0 = (wave * C::LPW + u) * C::RPI;
+      const int row = row0 + ld_row_in;
+      const uint32_t g = (uint32_t)(t * C::BC + row) * RB + 16u * (ld_chunk ^ swz_v<D>(row));
+      load_lds16(vrs, smem + lds_off + row0 * RB, g);
     }
   };
 
-  // ---- per-lane read offsets
+  // ---- per-lane LDS offsets, hoisted out of the loop.  Rows 16 and 32 apart
+  // share a swizzle, so tile/row/buffer displacements are compile-time constants.
   // score A operand: K row 32*kt + swap_bits23(l32), logical chunk 2*ks + half
-  const int krow = swap_bits23(l32);
-  // value A operand (transposed read): lane j = l & 15 of its group addresses
-  // row key0 + (j >> 2), column cbase + 4 * (j & 3); cbase = 32*ct + 16*((l >> 4) & 1)
-  const int tr_t = (lane & 15) >> 2;
-  const int tr_q = lane & 3;
-  const int tr_cb = 16 * ((lane >> 4) & 1);
+  int koff[C::KSTEPS];
+  {
+    const int r = swap_bits23(l32);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) koff[ks] = r * RB + 16 * ((2 * ks + half) ^ swz_k<D>(r));
+  }
+  // value A operand (transposed read): lane j = l & 15 of its 16-lane group
+  // addresses row key0 + (j >> 2), columns 32*ct + 16*((l >> 4) & 1) + 4*(j & 3)
+  uint32_t voff[C::CT][2];
+  {
+    const uint32_t vb = lds_addr(smem) + 2 * TB;
+    const int rlo = 8 * half + ((lane & 15) >> 2);
+    const int tq = lane & 3;
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+      const int ch = 4 * ct + 2 * ((lane >> 4) & 1) + (tq >> 1);
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = rlo + 4 * hi;
+        voff[ct][hi] = vb + r * RB + 16 * (ch ^ swz_v<D>(r)) + 8 * (tq & 1);
+      }
+    }
+  }
 
   floatx16 oacc[C::CT];
 #pragma unroll
@@ -165,61 +194,57 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   float m_ref = -INFINITY;  // running reference maximum of raw scores q.k
   float l_part = 0.f;       // this lane's part of the running exponential sum
 
-  issue_tile(0, 0);
+  // S^T of one 32-key sub-tile, k-steps [k0, k0 + n) into acc
+  auto qk_steps = [&](floatx16 &acc, const unsigned char *kbuf, int kt, int k0, int n) {
+    bf16x8 a[C::KSTEPS];
+#pragma unroll
+    for (int i = 0; i < C::KSTEPS; ++i)
+      if (i < n) a[i] = as_bf16x8(ld16(kbuf + koff[k0 + i] + 32 * kt * RB));
+#pragma unroll
+    for (int i = 0; i < C::KSTEPS; ++i)
+      if (i < n) acc = mfma32x32x16(a[i], qf[k0 + i], acc);
+  };
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  constexpr int NCH = 2 * C::NKT;            // P chunks of 8 keys per lane per tile
+  constexpr int QK_PER_CH = C::KSTEPS / 2;   // score MFMAs of the next tile per chunk
+
+  // One tile step.  BUF is the V buffer of tile t (and the K buffer of tile t).
+  auto step = [&](auto bufc, int t, floatx16 (&cur)[C::NKT], floatx16 (&nxt)[C::NKT]) {
+    constexpr int BUF = decltype(bufc)::value;
     wait_vmem();
-    __syncthreads();  // tile t is in LDS for everyone; tile t-1 is no longer read
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    __syncthreads();  // K(t+1) and V(t) are in LDS; nobody reads K(t) or V(t-1) any more
+    if (t + 2 < ntiles) issue_k(t + 2, BUF * TB);
+    if (t + 1 < ntiles) issue_v(t + 1, (2 + (BUF ^ 1)) * TB);
 
     const int kb = t * C::BC;
-    const bool wave_active = !CAUSAL || (kb <= qw0 + 31);
-    if (wave_active) {
-      const unsigned char *Ks = smem + buf * C::STAGE_BYTES;
-      const uint32_t vbase_addr = lds_addr(Ks + C::TILE_BYTES);
+    const bool act = !CAUSAL || (kb <= qw0 + 31);
+    const bool act_n = (t + 1 < ntiles) && (!CAUSAL || (kb + C::BC <= qw0 + 31));
+    const unsigned char *knext = smem + (BUF ^ 1) * TB;
 
-      // ---- S^T = K Q^T for NKT tiles of 32 keys
-      floatx16 s[C::NKT];
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt) {
-        const int r = 32 * kt + krow;
-        const unsigned char *rowp = Ks + r * C::ROW_BYTES;
-        const int sw = swz_k<D>(r);
-        bf16x8 a[C::KSTEPS];
-#pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) a[ks] = as_bf16x8(ld16(rowp + 16 * ((2 * ks + half) ^ sw)));
-        s[kt] = floatx16{0};
-#pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) s[kt] = mfma32x32x16(a[ks], qf[ks], s[kt]);
-      }
-
+    float mc = 0.f;
+    if (act) {
       // ---- masking (diagonal and ragged tiles only)
       const bool need_mask = (CAUSAL && (kb + C::BC - 1 > qw0)) || (kb + C::BC > N);
       if (need_mask) {
 #pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt) {
+        for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kb + 32 * kt + 16 * (r >> 3) + 8 * half + (r & 7);
-            const bool hide = (key >= N) || (CAUSAL && key > my_q);
-            if (hide) s[kt][r] = -INFINITY;
+            if ((key >= N) || (CAUSAL && key > my_q)) cur[kt][r] = -INFINITY;
           }
-        }
       }
-
-      // ---- row maximum of this tile
-      float mloc = s[0][0];
+      // ---- row maximum of tile t
+      float mloc = max3f(cur[0][0], cur[0][1], cur[0][2]);
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-        for (int r = (kt == 0 ? 1 : 0); r < 16; r += 2) {
-          if (r + 1 < 16) mloc = fmaxf(mloc, fmaxf(s[kt][r], s[kt][r + 1]));
-          else mloc = fmaxf(mloc, s[kt][r]);
+        for (int r = (kt == 0 ? 3 : 0); r < 16; r += 2) {
+          if (r + 1 < 16) mloc = max3f(mloc, cur[kt][r], cur[kt][r + 1]);
+          else mloc = fmaxf(mloc, cur[kt][r]);
         }
       const float m_tile = max_with_partner(mloc);
       const float m_new = fmaxf(m_ref, m_tile);
-
       // ---- move the reference maximum only when the scores outgrow it by > 2^8
       const bool grow = (m_new - m_ref) * scale_log2e > 8.0f;
       if (__ballot(grow) != 0) {
@@ -231,44 +256,74 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[ct][r] *= alpha;
       }
-      const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * scale_log2e;
-
-      // ---- P = 2^(S c - m c) in bf16, its row sum, and O^T += V^T P^T
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          u32x4 pw;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[kt][8 * m + 2 * i], scale_log2e, -mc));
-            const float p1 = fast_exp2(__builtin_fmaf(s[kt][8 * m + 2 * i + 1], scale_log2e, -mc));
-            pw[i] = pack_bf16x2(p0, p1);
-            l_part = add_bf16_pair(pw[i], l_part);
-          }
-          const bf16x8 pb = as_bf16x8(pw);
-          const int key0 = 32 * kt + 16 * m + 8 * half + tr_t;
-          const uint32_t a_lo = vbase_addr + key0 * C::ROW_BYTES + 8 * (tr_q & 1);
-          const uint32_t a_hi = a_lo + 4 * C::ROW_BYTES;
-          const int sw_lo = swz_v<D>(key0), sw_hi = swz_v<D>(key0 + 4);
-#pragma unroll
-          for (int c2 = 0; c2 < C::CT; c2 += 2) {
-            // two 32-column tiles per batch: four transposed reads, one wait
-            const int ch0 = (32 * c2 + tr_cb) / 8 + (tr_q >> 1);
-            const int ch1 = ch0 + 4;
-            u32x2 l0 = ds_read_tr16(a_lo + 16 * (ch0 ^ sw_lo));
-            u32x2 h0 = ds_read_tr16(a_hi + 16 * (ch0 ^ sw_hi));
-            u32x2 l1 = ds_read_tr16(a_lo + 16 * (ch1 ^ sw_lo));
-            u32x2 h1 = ds_read_tr16(a_hi + 16 * (ch1 ^ sw_hi));
-            lds_wait(l0, h0, l1, h1);
-            const u32x4 a0 = {l0[0], l0[1], h0[0], h0[1]};
-            const u32x4 a1 = {l1[0], l1[1], h1[0], h1[1]};
-            oacc[c2] = mfma32x32x16(as_bf16x8(a0), pb, oacc[c2]);
-            oacc[c2 + 1] = mfma32x32x16(as_bf16x8(a1), pb, oacc[c2 + 1]);
-          }
-        }
-      }
+      mc = (m_ref == -INFINITY) ? 0.f : m_ref * scale_log2e;
     }
+
+    // ---- P of tile t, O^T += V^T P^T, interleaved with S^T of tile t+1
+    auto chunk_p = [&](int kt, int m) -> bf16x8 {
+      u32x4 pw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = fast_exp2(__builtin_fmaf(cur[kt][8 * m + 2 * i], scale_log2e, -mc));
+        const float p1 = fast_exp2(__builtin_fmaf(cur[kt][8 * m + 2 * i + 1], scale_log2e, -mc));
+        pw[i] = pack_bf16x2(p0, p1);
+        l_part = add_bf16_pair(pw[i], l_part);
+      }
+      return as_bf16x8(pw);
+    };
+    auto chunk_pv = [&](auto cc, const bf16x8 &pb) {
+      constexpr int CH = decltype(cc)::value;
+      constexpr int ROWOFF = BUF * TB + (16 * CH) * RB;  // kt = CH/2, m = CH%2: row 32kt + 16m = 16*CH
+#pragma unroll
+      for (int c2 = 0; c2 < C::CT; c2 += 2) {
+        u32x2 l0 = ds_read_tr16_at<ROWOFF>(voff[c2][0]);
+        u32x2 h0 = ds_read_tr16_at<ROWOFF>(voff[c2][1]);
+        u32x2 l1 = ds_read_tr16_at<ROWOFF>(voff[c2 + 1][0]);
+        u32x2 h1 = ds_read_tr16_at<ROWOFF>(voff[c2 + 1][1]);
+        lds_wait(l0, h0, l1, h1);
+        const u32x4 a0 = {l0[0], l0[1], h0[0], h0[1]};
+        const u32x4 a1 = {l1[0], l1[1], h1[0], h1[1]};
+        oacc[c2] = mfma32x32x16(as_bf16x8(a0), pb, oacc[c2]);
+        oacc[c2 + 1] = mfma32x32x16(as_bf16x8(a1), pb, oacc[c2 + 1]);
+      }
+    };
+    auto chunk_qk = [&](int ch) {
+      // score MFMAs [ch * QK_PER_CH, +QK_PER_CH) of tile t+1, kt-major
+      const int first = ch * QK_PER_CH;
+      const int kt = first / C::KSTEPS;
+      const int k0 = first % C::KSTEPS;
+      if (k0 == 0) nxt[kt] = floatx16{0};
+      qk_steps(nxt[kt], knext, kt, k0, QK_PER_CH);
+    };
+
+    // (a wave that is active for tile t but not for t+1 -- the last tile, or
+    // the causal diagonal -- computes scores it will not use; they are discarded)
+    if (act) {
+      static_for<NCH>([&](auto cc) {
+        constexpr int CH = decltype(cc)::value;
+        const bf16x8 pb = chunk_p(CH / 2, CH % 2);
+        chunk_qk(CH);
+        chunk_pv(cc, pb);
+      });
+    }
+  };
+
+  // ---- prologue: K(0), V(0), K(1) in flight, then S of tile 0
+  issue_k(0, 0);
+  issue_v(0, 2 * TB);
+  if (ntiles > 1) issue_k(1, TB);
+  floatx16 sA[C::NKT], sB[C::NKT];
+  wait_vmem();
+  __syncthreads();
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt) {
+    sA[kt] = floatx16{0};
+    qk_steps(sA[kt], smem, kt, 0, C::KSTEPS);
+  }
+
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, t, sA, sB);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1, sB, sA);
   }
 
   // ---- epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
