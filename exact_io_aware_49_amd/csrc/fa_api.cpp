@@ -74,7 +74,8 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
   if (check_common(B, H, N, d, 0, 1.0f, dtype) != FA_OK || dtype != FA_DTYPE_BF16) return 0;
-  const size_t bytes = (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  // D_i and lse_i * log2(e), one float32 each per query row
+  const size_t bytes = 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
 }
 

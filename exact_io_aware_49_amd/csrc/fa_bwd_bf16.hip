@@ -10,58 +10,143 @@
 //
 // Two kernels, no atomics:
 //   fa_bwd_dq_kernel   -- owns 128 query rows (32 per wave).  Computes D for its
-//                         rows (stored for the second kernel), then streams K/V
-//                         tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+//                         rows and stores D and lse*log2(e) for the second kernel,
+//                         then streams K/V tiles of 64 keys:
+//                         S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
 //                         Lane = query row, so lse and D are per-lane scalars.
 //   fa_bwd_dkdv_kernel -- owns 128 keys (32 per wave), K and V rows held in
-//                         registers.  Streams query tiles: S = Q K^T, dP = dO V^T,
-//                         dS, dV^T += dO^T P, dK^T += Q^T dS.  Lane = key.
-// The second product of each kernel needs its streamed operand transposed
-// (K^T, dO^T, Q^T); those copies are written to LDS by the staging threads,
-// with the 4x8 register transpose of fa_device.h.  P and dS go straight from
-// the accumulator registers of the first products into the B operand of the
-// second ones (row order fixed by swap_bits23), so they never touch LDS.
+//                         registers.  Streams Q/dO tiles of 64 queries:
+//                         S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
+//                         Lane = key.
+// Streamed tiles go from HBM straight into LDS (buffer_load ... lds, double
+// buffered) as row-major tiles whose 16-byte chunks are XOR-permuted per row.
+// Each tile is read twice from that single copy: as rows (ds_read_b128, the A
+// operand of the first products) and transposed (ds_read_b64_tr_b16, the A
+// operand of the second products).  P and dS go straight from the accumulator
+// registers of the first products into the B operand of the second ones (row
+// order fixed by swap_bits23), so they never touch LDS.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-// ============================================================== dQ kernel
 template <int D>
-struct DqCfg {
-  static constexpr int BR = 128;              // query rows per workgroup
-  static constexpr int BC = 64;               // keys per tile
-  static constexpr int NKT = BC / 32;
+struct BwdCfg {
+  static constexpr int TROWS = 64;            // rows of a streamed tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int CT = D / 32;
-  static constexpr int RSTRIDE = D + 8;       // K and V rows in LDS
-  static constexpr int TSTRIDE = BC + 8;      // K^T rows in LDS
-  static constexpr int KT_ELEMS = BC * RSTRIDE;
-  static constexpr int KTT_ELEMS = D * TSTRIDE;
-  static constexpr int STAGE = 2 * KT_ELEMS + KTT_ELEMS;
-  static constexpr int UNITS = (BC / 4) * (D / 8);  // 4x8 blocks per operand tile
-  static constexpr int MINW = (D == 64) ? 2 : 1;
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int RB = 2 * D;            // bytes per row
+  static constexpr int RPI = 1024 / RB;       // rows per wave-wide 16-byte load
+  static constexpr int TB = TROWS * RB;       // bytes per tile
+  static constexpr int LPW = TB / 1024 / 4;   // loads per wave per tile
 };
 
+// One 64-row tile of a [N, D] head slab (rows r0 .. r0+63) into LDS at `dst`,
+// split over the 4 waves; rows past N read as zero.
+template <int D>
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, int r0, int wave,
+                                           int lane) {
+  using C = BwdCfg<D>;
+#pragma unroll
+  for (int u = 0; u < C::LPW; ++u) {
+    const int row0 = (wave * C::LPW + u) * C::RPI;
+    const int row = row0 + lane / C::CPR;
+    const uint32_t g = (uint32_t)(r0 + row) * C::RB + 16u * ((lane % C::CPR) ^ swz_rt<D>(row));
+    load_lds16(rs, dst + row0 * C::RB, g);
+  }
+}
+
+// Per-lane byte offsets of the two read patterns of a tile.
+//  rows : A operand of a 32x32x16 MFMA over 32 tile rows 32*sub + swap_bits23(l32),
+//         k-step ks -> logical chunk 2*ks + half.  Add 32*sub*RB for sub-tile `sub`.
+//  trans: transposed read (ds_read_b64_tr_b16) of rows 16*ch + 8*half + (l&15)/4 (+4 for
+//         the high half), columns 32*ct + 16*((l>>4)&1) + 4*(l&3).  Add 16*ch*RB.
+template <int D>
+struct TileOffsets {
+  int rows[D / 16];
+  uint32_t trans[D / 32][2];
+  __device__ __forceinline__ void init(int lane, uint32_t trans_base) {
+    using C = BwdCfg<D>;
+    const int half = lane >> 5;
+    const int r = swap_bits23(lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) rows[ks] = r * C::RB + 16 * ((2 * ks + half) ^ swz_rt<D>(r));
+    const int rlo = 8 * half + ((lane & 15) >> 2);
+    const int tq = lane & 3;
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+      const int ch = 4 * ct + 2 * ((lane >> 4) & 1) + (tq >> 1);
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int rr = rlo + 4 * hi;
+        trans[ct][hi] = trans_base + rr * C::RB + 16 * (ch ^ swz_rt<D>(rr)) + 8 * (tq & 1);
+      }
+    }
+  }
+};
+
+// acc[ct] += A^T(ct) * b, where A^T(ct) is the transposed read of the tile at
+// LDS displacement OFF (buffer base + 16*ch*RB) for 32-column group ct.
+template <int D, int OFF>
+__device__ __forceinline__ void mfma_transposed(floatx16 (&acc)[D / 32], const TileOffsets<D> &to,
+                                                const bf16x8 &b) {
+#pragma unroll
+  for (int c2 = 0; c2 < D / 32; c2 += 2) {
+    u32x2 l0 = ds_read_tr16_at<OFF>(to.trans[c2][0]);
+    u32x2 h0 = ds_read_tr16_at<OFF>(to.trans[c2][1]);
+    u32x2 l1 = ds_read_tr16_at<OFF>(to.trans[c2 + 1][0]);
+    u32x2 h1 = ds_read_tr16_at<OFF>(to.trans[c2 + 1][1]);
+    lds_wait(l0, h0, l1, h1);
+    const u32x4 a0 = {l0[0], l0[1], h0[0], h0[1]};
+    const u32x4 a1 = {l1[0], l1[1], h1[0], h1[1]};
+    acc[c2] = mfma32x32x16(as_bf16x8(a0), b, acc[c2]);
+    acc[c2 + 1] = mfma32x32x16(as_bf16x8(a1), b, acc[c2 + 1]);
+  }
+}
+
+// Store a [32 rows x D] fp32 accumulator (lane = row l32, register r of column
+// tile ct = column 32*ct + 8*(r/4) + 4*half + r%4) as bf16 times `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows_bf16(__bf16 *row, const floatx16 (&acc)[D / 32], float mul, int half) {
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[ct][4 * g + 0] * mul, acc[ct][4 * g + 1] * mul);
+      w[1] = pack_bf16x2(acc[ct][4 * g + 2] * mul, acc[ct][4 * g + 3] * mul);
+      st8(row + 32 * ct + 8 * g + 4 * half, w);
+    }
+  }
+}
+
+// ============================================================== dQ kernel
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, DqCfg<D>::MINW)
+__global__ void __launch_bounds__(256, 2)
 fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                  const __bf16 *__restrict__ Og, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
-                 __bf16 *__restrict__ dQ, float *__restrict__ Dsum, int N, float scale_log2e, float scale) {
-  using C = DqCfg<D>;
-  __shared__ __align__(16) __bf16 smem[2 * C::STAGE];
+                 __bf16 *__restrict__ dQ, float *__restrict__ Dsum, float *__restrict__ Lse2, int N,
+                 float scale_log2e, float scale) {
+  using C = BwdCfg<D>;
+  constexpr int TB = C::TB;
+  constexpr int RB = C::RB;
+  constexpr int BR = 128;  // query rows per workgroup
+  // LDS: K tiles at [0, TB), [TB, 2TB); V tiles at [2TB, 3TB), [3TB, 4TB)
+  __shared__ __align__(1024) unsigned char smem[4 * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int nqb = (N + C::BR - 1) / C::BR;
-  const int bh = blockIdx.x % (gridDim.x / nqb);
-  const int qb = CAUSAL ? (nqb - 1 - blockIdx.x / (gridDim.x / nqb)) : (blockIdx.x / (gridDim.x / nqb));
+  const int nqb = (N + BR - 1) / BR;
+  const int nbh = gridDim.x / nqb;
+  const int bh = blockIdx.x % nbh;
+  const int qb = CAUSAL ? (nqb - 1 - (int)blockIdx.x / nbh) : ((int)blockIdx.x / nbh);
   const size_t head_off = (size_t)bh * N * D;
-  const int q0 = qb * C::BR;
+  const int q0 = qb * BR;
   const int qw0 = q0 + 32 * wave;
   const int my_q = qw0 + l32;
   const bool q_ok = my_q < N;
@@ -88,150 +173,110 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
   }
   const float drow = sum_with_partner(dpart);
   const float lse2 = q_ok ? LSE[(size_t)bh * N + my_q] * kLog2e : 0.f;
-  if (q_ok && half == 0) Dsum[(size_t)bh * N + my_q] = drow;
+  if (q_ok && half == 0) {
+    Dsum[(size_t)bh * N + my_q] = drow;
+    Lse2[(size_t)bh * N + my_q] = lse2;
+  }
 
-  int ntiles = (N + C::BC - 1) / C::BC;
-  if (CAUSAL) ntiles = min(ntiles, (min(q0 + C::BR, N) - 1) / C::BC + 1);
+  int ntiles = (N + 63) / 64;
+  if (CAUSAL) ntiles = min(ntiles, (min(q0 + BR, N) - 1) / 64 + 1);
 
-  // ---- staging: K unit (rows + transposed) and V unit (rows) per thread
-  const bool do_k = (C::UNITS == 256) || (tid < 128);
-  const bool do_v = (C::UNITS == 256) || (tid >= 128);
-  const int unit = (C::UNITS == 256) ? tid : (tid & 127);
-  const int u_kq = unit % (C::BC / 4);
-  const int u_g = unit / (C::BC / 4);
-  const __bf16 *Kh = K + head_off;
-  const __bf16 *Vh = V + head_off;
-  u32x4 kblk[4], vblk[4];
-
-  auto load_tile = [&](int t) {
-    const int kb = t * C::BC;
-    if (do_k) load_block4x8(kblk, Kh, kb + 4 * u_kq, N, D, u_g);
-    if (do_v) load_block4x8(vblk, Vh, kb + 4 * u_kq, N, D, u_g);
-  };
-  auto store_tile = [&](int buf) {
-    __bf16 *Ks = smem + buf * C::STAGE;
-    __bf16 *Vs = Ks + C::KT_ELEMS;
-    __bf16 *KTs = Vs + C::KT_ELEMS;
-    if (do_k) {
-      store_block_rows(Ks, C::RSTRIDE, 4 * u_kq, u_g, kblk);
-      store_block_transposed(KTs, C::TSTRIDE, 4 * u_kq, u_g, kblk);
-    }
-    if (do_v) store_block_rows(Vs, C::RSTRIDE, 4 * u_kq, u_g, vblk);
-  };
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + head_off, head_bytes);
+  TileOffsets<D> to;
+  to.init(lane, lds_addr(smem));  // transposed reads are of the K tiles
 
   floatx16 dqacc[C::CT];
 #pragma unroll
   for (int ct = 0; ct < C::CT; ++ct) dqacc[ct] = floatx16{0};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  const int arow = swap_bits23(l32);
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool prefetch = (t + 1) < ntiles;
-    if (prefetch) load_tile(t + 1);
-    const int kb = t * C::BC;
-    if (!CAUSAL || kb <= qw0 + 31) {
-      const __bf16 *Ks = smem + buf * C::STAGE;
-      const __bf16 *Vs = Ks + C::KT_ELEMS;
-      const __bf16 *KTs = Vs + C::KT_ELEMS;
-      floatx16 s[C::NKT], dp[C::NKT];
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt) {
-        s[kt] = floatx16{0};
-        dp[kt] = floatx16{0};
-        const __bf16 *krow = Ks + (32 * kt + arow) * C::RSTRIDE + 8 * half;
-        const __bf16 *vrow = Vs + (32 * kt + arow) * C::RSTRIDE + 8 * half;
+  auto step = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    wait_vmem();
+    __syncthreads();  // tile t is in LDS for everyone; tile t-1 is no longer read
+    if (t + 1 < ntiles) {
+      issue_tile<D>(krs, smem + (BUF ^ 1) * TB, (t + 1) * 64, wave, lane);
+      issue_tile<D>(vrs, smem + (2 + (BUF ^ 1)) * TB, (t + 1) * 64, wave, lane);
+    }
+    const int kb = t * 64;
+    if (CAUSAL && kb > qw0 + 31) return;  // every key of the tile is above this wave's rows
+    const unsigned char *Ks = smem + BUF * TB;
+    const unsigned char *Vs = smem + (2 + BUF) * TB;
+    const bool need_mask = (CAUSAL && (kb + 63 > qw0)) || (kb + 64 > N);
+    static_for<2>([&](auto ktc) {
+      constexpr int KT = decltype(ktc)::value;
+      floatx16 s = floatx16{0}, dp = floatx16{0};
+      {
+        bf16x8 a[C::KSTEPS], b[C::KSTEPS];
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
-          s[kt] = mfma32x32x16(as_bf16x8(ld16(krow + 16 * ks)), qf[ks], s[kt]);
-          dp[kt] = mfma32x32x16(as_bf16x8(ld16(vrow + 16 * ks)), dof[ks], dp[kt]);
+          a[ks] = as_bf16x8(ld16(Ks + to.rows[ks] + 32 * KT * RB));
+          b[ks] = as_bf16x8(ld16(Vs + to.rows[ks] + 32 * KT * RB));
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+          s = mfma32x32x16(a[ks], qf[ks], s);
+          dp = mfma32x32x16(b[ks], dof[ks], dp);
         }
       }
-      const bool need_mask = (CAUSAL && (kb + C::BC - 1 > qw0)) || (kb + C::BC > N);
+      static_for<2>([&](auto mc) {
+        constexpr int M = decltype(mc)::value;
+        u32x4 w;
 #pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt) {
+        for (int i = 0; i < 4; ++i) {
+          float d2[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          float d8[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int r = 8 * m + i;
-            float p = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2e, -lse2));
+          for (int e = 0; e < 2; ++e) {
+            const int r = 8 * M + 2 * i + e;
+            float p = fast_exp2(__builtin_fmaf(s[r], scale_log2e, -lse2));
             if (need_mask) {
-              const int key = kb + 32 * kt + 16 * m + 8 * half + i;
+              const int key = kb + 32 * KT + 16 * M + 8 * half + 2 * i + e;
               if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
             }
-            d8[i] = p * (dp[kt][r] - drow);
+            d2[e] = p * (dp[r] - drow);
           }
-          const bf16x8 dsb = to_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
-          const int key_off = 32 * kt + 16 * m + 8 * half;
-#pragma unroll
-          for (int ct = 0; ct < C::CT; ++ct) {
-            const bf16x8 a = as_bf16x8(ld16(KTs + (32 * ct + l32) * C::TSTRIDE + key_off));
-            dqacc[ct] = mfma32x32x16(a, dsb, dqacc[ct]);
-          }
+          w[i] = pack_bf16x2(d2[0], d2[1]);
         }
-      }
-    }
-    if (prefetch) store_tile(buf ^ 1);
-    __syncthreads();
+        mfma_transposed<D, BUF * TB + 16 * (2 * KT + M) * RB>(dqacc, to, as_bf16x8(w));
+      });
+    });
+  };
+
+  issue_tile<D>(krs, smem, 0, wave, lane);
+  issue_tile<D>(vrs, smem + 2 * TB, 0, wave, lane);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  if (q_ok) {
-    __bf16 *row = dQ + head_off + (size_t)my_q * D;
-#pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack_bf16x2(dqacc[ct][4 * g + 0] * scale, dqacc[ct][4 * g + 1] * scale);
-        w[1] = pack_bf16x2(dqacc[ct][4 * g + 2] * scale, dqacc[ct][4 * g + 3] * scale);
-        st8(row + 32 * ct + 8 * g + 4 * half, w);
-      }
-    }
-  }
+  if (q_ok) store_rows_bf16<D>(dQ + head_off + (size_t)my_q * D, dqacc, scale, half);
 }
 
 // ============================================================== dK/dV kernel
-template <int D>
-struct DkvCfg {
-  static constexpr int BKV = 128;             // keys per workgroup
-  static constexpr int BQ = 64;               // query rows per tile
-  static constexpr int NQT = BQ / 32;
-  static constexpr int KSTEPS = D / 16;
-  static constexpr int CT = D / 32;
-  static constexpr int RSTRIDE = D + 8;       // Q and dO rows in LDS
-  static constexpr int TSTRIDE = BQ + 8;      // Q^T and dO^T rows in LDS
-  static constexpr int R_ELEMS = BQ * RSTRIDE;
-  static constexpr int T_ELEMS = D * TSTRIDE;
-  static constexpr int STAGE = 2 * R_ELEMS + 2 * T_ELEMS + 2 * BQ * 2;  // + lse, D as float
-  static constexpr int UNITS = (BQ / 4) * (D / 8);
-  static constexpr int MINW = (D == 64) ? 2 : 1;
-};
-
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, DkvCfg<D>::MINW)
+__global__ void __launch_bounds__(256, (D == 64) ? 2 : 1)
 fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
-                   const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
-                   const float *__restrict__ Dsum, __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N,
-                   float scale_log2e, float scale) {
-  using C = DkvCfg<D>;
-  __shared__ __align__(16) __bf16 smem[2 * C::STAGE];
+                   const __bf16 *__restrict__ dO, const float *__restrict__ Dsum, const float *__restrict__ Lse2,
+                   __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N, float scale_log2e, float scale) {
+  using C = BwdCfg<D>;
+  constexpr int TB = C::TB;
+  constexpr int RB = C::RB;
+  constexpr int BKV = 128;                  // keys per workgroup
+  constexpr int STAGE = 2 * TB + 1024;      // Q tile, dO tile, lse*log2e[64], D[64]
+  __shared__ __align__(1024) unsigned char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int nkb = (N + C::BKV - 1) / C::BKV;
+  const int nkb = (N + BKV - 1) / BKV;
   const int nbh = gridDim.x / nkb;
   const int bh = blockIdx.x % nbh;
   const int kblk = blockIdx.x / nbh;  // ascending: with a causal mask the first blocks have the most work
   const size_t head_off = (size_t)bh * N * D;
-  const int kb0 = kblk * C::BKV;
+  const int kb0 = kblk * BKV;
   const int kw0 = kb0 + 32 * wave;
   const int my_k = kw0 + l32;
   const bool k_ok = my_k < N;
@@ -247,48 +292,23 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
     }
   }
 
-  const int nqt_all = (N + C::BQ - 1) / C::BQ;
-  const int qt0 = CAUSAL ? (kb0 / C::BQ) : 0;
+  const int nqt = (N + 63) / 64;
+  const int qt0 = CAUSAL ? (kb0 / 64) : 0;
 
-  const bool do_q = (C::UNITS == 256) || (tid < 128);
-  const bool do_o = (C::UNITS == 256) || (tid >= 128);
-  const int unit = (C::UNITS == 256) ? tid : (tid & 127);
-  const int u_kq = unit % (C::BQ / 4);
-  const int u_g = unit / (C::BQ / 4);
-  const __bf16 *Qh = Q + head_off;
-  const __bf16 *dOh = dO + head_off;
-  const float *Lh = LSE + (size_t)bh * N;
-  const float *Dh = Dsum + (size_t)bh * N;
-  u32x4 qblk[4], oblk[4];
-  float lsv = 0.f;
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(Lse2 + (size_t)bh * N, (uint32_t)N * 4u);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(Dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  TileOffsets<D> to;
+  to.init(lane, lds_addr(smem));  // transposed reads of the Q tile; the dO tile is TB further
 
-  auto load_tile = [&](int t) {
-    const int qs = t * C::BQ;
-    if (do_q) load_block4x8(qblk, Qh, qs + 4 * u_kq, N, D, u_g);
-    if (do_o) load_block4x8(oblk, dOh, qs + 4 * u_kq, N, D, u_g);
-    if (tid < C::BQ) {
-      const int q = qs + tid;
-      lsv = (q < N) ? Lh[q] * kLog2e : INFINITY;  // rows past N get P = 0
-    } else if (tid < 2 * C::BQ) {
-      const int q = qs + tid - C::BQ;
-      lsv = (q < N) ? Dh[q] : 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) {
-    __bf16 *Qs = smem + buf * C::STAGE;
-    __bf16 *dOs = Qs + C::R_ELEMS;
-    __bf16 *QTs = dOs + C::R_ELEMS;
-    __bf16 *dOTs = QTs + C::T_ELEMS;
-    float *stat = reinterpret_cast<float *>(dOTs + C::T_ELEMS);  // [0, BQ): lse*log2e, [BQ, 2BQ): D
-    if (do_q) {
-      store_block_rows(Qs, C::RSTRIDE, 4 * u_kq, u_g, qblk);
-      store_block_transposed(QTs, C::TSTRIDE, 4 * u_kq, u_g, qblk);
-    }
-    if (do_o) {
-      store_block_rows(dOs, C::RSTRIDE, 4 * u_kq, u_g, oblk);
-      store_block_transposed(dOTs, C::TSTRIDE, 4 * u_kq, u_g, oblk);
-    }
-    if (tid < 2 * C::BQ) stat[tid] = lsv;
+  auto issue = [&](int t, int stage) {
+    unsigned char *base = smem + stage * STAGE;
+    issue_tile<D>(qrs, base, t * 64, wave, lane);
+    issue_tile<D>(ors, base + TB, t * 64, wave, lane);
+    if (wave == 0) load_lds4(lrs, base + 2 * TB, (uint32_t)(t * 64 + lane) * 4u);
+    if (wave == 1) load_lds4(drs, base + 2 * TB + 256, (uint32_t)(t * 64 + lane) * 4u);
   };
 
   floatx16 dkacc[C::CT], dvacc[C::CT];
@@ -298,121 +318,111 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
     dvacc[ct] = floatx16{0};
   }
 
-  const int arow = swap_bits23(l32);
-  if (qt0 < nqt_all) {
-    load_tile(qt0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = qt0; t < nqt_all; ++t) {
-    const int buf = (t - qt0) & 1;
-    const bool prefetch = (t + 1) < nqt_all;
-    if (prefetch) load_tile(t + 1);
-    const int qs = t * C::BQ;
-    if (!CAUSAL || qs + C::BQ - 1 >= kw0) {
-      const __bf16 *Qs = smem + buf * C::STAGE;
-      const __bf16 *dOs = Qs + C::R_ELEMS;
-      const __bf16 *QTs = dOs + C::R_ELEMS;
-      const __bf16 *dOTs = QTs + C::T_ELEMS;
-      const float *stat = reinterpret_cast<const float *>(dOTs + C::T_ELEMS);
-      const bool need_mask = (CAUSAL && qs < kw0 + 31) || (kb0 + C::BKV > N);
-#pragma unroll
-      for (int qt = 0; qt < C::NQT; ++qt) {
-        floatx16 s = floatx16{0}, dp = floatx16{0};
-        const __bf16 *qrow = Qs + (32 * qt + arow) * C::RSTRIDE + 8 * half;
-        const __bf16 *orow = dOs + (32 * qt + arow) * C::RSTRIDE + 8 * half;
+  auto step = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < nqt) issue(t + 1, BUF ^ 1);
+    const int qs = t * 64;
+    if (CAUSAL && qs + 63 < kw0) return;  // every query of the tile is before this wave's keys
+    const unsigned char *Qs = smem + BUF * STAGE;
+    const unsigned char *Os = Qs + TB;
+    const float *lst = reinterpret_cast<const float *>(Qs + 2 * TB);
+    const bool need_mask = (CAUSAL && qs < kw0 + 31) || (qs + 64 > N) || (kb0 + BKV > N);
+    static_for<2>([&](auto qtc) {
+      constexpr int QT = decltype(qtc)::value;
+      floatx16 s = floatx16{0}, dp = floatx16{0};
+      {
+        bf16x8 a[C::KSTEPS], b[C::KSTEPS];
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
-          s = mfma32x32x16(as_bf16x8(ld16(qrow + 16 * ks)), kf[ks], s);
-          dp = mfma32x32x16(as_bf16x8(ld16(orow + 16 * ks)), vf[ks], dp);
+          a[ks] = as_bf16x8(ld16(Qs + to.rows[ks] + 32 * QT * RB));
+          b[ks] = as_bf16x8(ld16(Os + to.rows[ks] + 32 * QT * RB));
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int qoff = 32 * qt + 16 * m + 8 * half;  // tile-local query of register 8m
-          const floatx4 l0 = *reinterpret_cast<const floatx4 *>(stat + qoff);
-          const floatx4 l1 = *reinterpret_cast<const floatx4 *>(stat + qoff + 4);
-          const floatx4 d0 = *reinterpret_cast<const floatx4 *>(stat + C::BQ + qoff);
-          const floatx4 d1 = *reinterpret_cast<const floatx4 *>(stat + C::BQ + qoff + 4);
-          float p8[8], s8[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float lq = (i < 4) ? l0[i] : l1[i - 4];
-            const float dq = (i < 4) ? d0[i] : d1[i - 4];
-            const int r = 8 * m + i;
-            float p = fast_exp2(__builtin_fmaf(s[r], scale_log2e, -lq));
-            if (need_mask) {
-              const int q = qs + qoff + i;
-              if (!k_ok || (CAUSAL && q < my_k)) p = 0.f;
-            }
-            p8[i] = p;
-            s8[i] = p * (dp[r] - dq);
-          }
-          const bf16x8 pb = to_bf16x8(p8[0], p8[1], p8[2], p8[3], p8[4], p8[5], p8[6], p8[7]);
-          const bf16x8 sb = to_bf16x8(s8[0], s8[1], s8[2], s8[3], s8[4], s8[5], s8[6], s8[7]);
-#pragma unroll
-          for (int ct = 0; ct < C::CT; ++ct) {
-            const bf16x8 ao = as_bf16x8(ld16(dOTs + (32 * ct + l32) * C::TSTRIDE + qoff));
-            const bf16x8 aq = as_bf16x8(ld16(QTs + (32 * ct + l32) * C::TSTRIDE + qoff));
-            dvacc[ct] = mfma32x32x16(ao, pb, dvacc[ct]);
-            dkacc[ct] = mfma32x32x16(aq, sb, dkacc[ct]);
-          }
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+          s = mfma32x32x16(a[ks], kf[ks], s);
+          dp = mfma32x32x16(b[ks], vf[ks], dp);
         }
       }
-    }
-    if (prefetch) store_tile(buf ^ 1);
-    __syncthreads();
+      static_for<2>([&](auto mc) {
+        constexpr int M = decltype(mc)::value;
+        const int qoff = 32 * QT + 16 * M + 8 * half;  // tile-local query of register 8M
+        const floatx4 l0 = *reinterpret_cast<const floatx4 *>(lst + qoff);
+        const floatx4 l1 = *reinterpret_cast<const floatx4 *>(lst + qoff + 4);
+        const floatx4 d0 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff);
+        const floatx4 d1 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff + 4);
+        u32x4 pw, sw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p2[2], s2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int j = 2 * i + e;
+            const float lq = (j < 4) ? l0[j] : l1[j - 4];
+            const float dq = (j < 4) ? d0[j] : d1[j - 4];
+            float p = fast_exp2(__builtin_fmaf(s[8 * M + j], scale_log2e, -lq));
+            if (need_mask) {
+              const int q = qs + qoff + j;
+              if (q >= N || !k_ok || (CAUSAL && q < my_k)) p = 0.f;
+            }
+            p2[e] = p;
+            s2[e] = p * (dp[8 * M + j] - dq);
+          }
+          pw[i] = pack_bf16x2(p2[0], p2[1]);
+          sw[i] = pack_bf16x2(s2[0], s2[1]);
+        }
+        constexpr int OFFQ = BUF * STAGE + 16 * (2 * QT + M) * RB;
+        mfma_transposed<D, OFFQ + TB>(dvacc, to, as_bf16x8(pw));  // dV^T += dO^T P
+        mfma_transposed<D, OFFQ>(dkacc, to, as_bf16x8(sw));       // dK^T += Q^T dS
+      });
+    });
+  };
+
+  if (qt0 < nqt) issue(qt0, 0);
+  for (int t = qt0; t < nqt; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nqt) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   if (k_ok) {
-    __bf16 *krow = dK + head_off + (size_t)my_k * D;
-    __bf16 *vrow = dV + head_off + (size_t)my_k * D;
-#pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dkacc[ct][4 * g + 0] * scale, dkacc[ct][4 * g + 1] * scale);
-        wk[1] = pack_bf16x2(dkacc[ct][4 * g + 2] * scale, dkacc[ct][4 * g + 3] * scale);
-        wv[0] = pack_bf16x2(dvacc[ct][4 * g + 0], dvacc[ct][4 * g + 1]);
-        wv[1] = pack_bf16x2(dvacc[ct][4 * g + 2], dvacc[ct][4 * g + 3]);
-        st8(krow + 32 * ct + 8 * g + 4 * half, wk);
-        st8(vrow + 32 * ct + 8 * g + 4 * half, wv);
-      }
-    }
+    store_rows_bf16<D>(dK + head_off + (size_t)my_k * D, dkacc, scale, half);
+    store_rows_bf16<D>(dV + head_off + (size_t)my_k * D, dvacc, 1.0f, half);
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                  const float *lse, void *dq, void *dk, void *dv, float *dsum, int B, int H, int N, float scale,
+                  const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int H, int N, float scale,
                   hipStream_t stream) {
   const long long nbh = (long long)B * H;
-  const long long gq = nbh * ((N + DqCfg<D>::BR - 1) / DqCfg<D>::BR);
-  const long long gk = nbh * ((N + DkvCfg<D>::BKV - 1) / DkvCfg<D>::BKV);
+  const long long gq = nbh * ((N + 127) / 128);
+  const long long gk = nbh * ((N + 127) / 128);
   if (gq > 0x7fffffffLL || gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = scale * kLog2e;
+  float *dsum = ws;
+  float *lse2 = ws + (size_t)nbh * N;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)gq), dim3(256), 0, stream,
                      (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)o,
-                     (const __bf16 *)dout, lse, (__bf16 *)dq, dsum, N, c, scale);
+                     (const __bf16 *)dout, lse, (__bf16 *)dq, dsum, lse2, N, c, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, stream,
-                     (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout, lse,
-                     (const float *)dsum, (__bf16 *)dk, (__bf16 *)dv, N, c, scale);
+                     (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
+                     (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, N, c, scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                           const float *lse, void *dq, void *dk, void *dv, float *dsum, int B, int H, int N,
+                           const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int H, int N,
                            int d, bool causal, float scale, hipStream_t stream) {
   if (d == 64)
-    return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, dsum, B, H, N, scale, stream)
-                  : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, dsum, B, H, N, scale, stream);
-  return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, dsum, B, H, N, scale, stream)
-                : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, dsum, B, H, N, scale, stream);
+    return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, stream)
+                  : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, stream);
+  return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, stream)
+                : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, stream);
 }
 
 }  // namespace fa

@@ -160,7 +160,22 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, void *ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, FA_LDS(void, lds_wave_base), 16, (int)voffset, 0, 0, 0);
 }
 
+// 4 bytes per lane into LDS at lds_wave_base + 4 * lane (buffer_load_dword ... lds).
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rsrc, void *lds_wave_base, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, FA_LDS(void, lds_wave_base), 4, (int)voffset, 0, 0, 0);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Chunk permutation for a row-major bf16 tile of d = 64 or 128 columns that is
+// read both as rows (16 consecutive rows, one 16-byte chunk each: the A operand
+// of a 32x32x16 MFMA) and transposed (ds_read_b64_tr_b16: 4 consecutive rows x
+// 4 chunks per 32 lanes).  physical chunk = logical chunk ^ swz_rt(row); both
+// patterns then hit 64 distinct banks.  Rows 16 apart share a permutation.
+template <int D>
+__device__ __forceinline__ int swz_rt(int r) {
+  return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

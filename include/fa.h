@@ -85,9 +85,9 @@ FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *l
            void *stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes: the per-row
- * D_i = sum_c dO_ic O_ic as float32 [B,H,N], rounded up to 256 bytes.
- * Returns 0 for arguments fa_bwd would reject.
+ * Bytes of device workspace fa_bwd needs for these sizes: per query row,
+ * D_i = sum_c dO_ic O_ic and lse_i * log2(e), float32 [2][B,H,N], rounded up
+ * to 256 bytes.  Returns 0 for arguments fa_bwd would reject.
  */
 FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
 
@@ -105,8 +105,9 @@ FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
  *                      and are garbage on exit.
  * Only FA_DTYPE_BF16 is supported (FA_ERR_UNSUPPORTED_DTYPE otherwise).
  * Two kernels run on `stream`: one owns a block of queries and produces dq
- * (and D), the other owns a block of keys and produces dk and dv.  No
- * atomics are used, so dq, dk and dv are bitwise reproducible.
+ * (and the per-row D and scaled lse in the workspace), the other owns a block
+ * of keys and produces dk and dv.  No atomics are used, so dq, dk and dv are
+ * bitwise reproducible.
  */
 FA_API int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            const void *dout, const float *lse, void *dq, void *dk, void *dv,

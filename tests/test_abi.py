@@ -81,7 +81,7 @@ def test_bwd_validation(kw, code):
 
 
 def test_workspace_size():
-    assert fa.fa_bwd_workspace_size(4, 16, 2048, 64, 1) == 4 * 16 * 2048 * 4
+    assert fa.fa_bwd_workspace_size(4, 16, 2048, 64, 1) == 2 * 4 * 16 * 2048 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 1) == 256
     assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 0) == 0   # fp32 backward unsupported
     assert fa.fa_bwd_workspace_size(1, 1, 3, 96, 1) == 0
