@@ -62,7 +62,7 @@ def compile_one(src: str, debug: bool) -> str:
     return obj
 
 
-def build(jobs: int = 4, debug: bool = False, verbose: bool = True) -> str:
+def build(jobs: int = 4, debug: bool = False, verbose: bool = True, check: bool = True) -> str:
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: compile_one(s, debug), SOURCES))
     tmp = LIB + ".tmp"
@@ -71,6 +71,12 @@ def build(jobs: int = 4, debug: bool = False, verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    if check:
+        from .check_isa import check_sources
+        bad = check_sources()
+        if bad:
+            os.remove(LIB)
+            raise RuntimeError("inline-asm LDS register hazards in the generated code:\n" + "\n".join(bad))
     if verbose:
         print(f"built {LIB}")
     return LIB

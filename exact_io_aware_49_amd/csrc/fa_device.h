@@ -205,6 +205,17 @@ __device__ __forceinline__ u32x2 ds_read_tr16_at(uint32_t addr) {
   return r;
 }
 
+// ds_read_b128 at addr + OFF, issued through inline asm (same contract as
+// ds_read_tr16: the caller guarantees completed transfers and waits with
+// lds_wait before use).
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+
 // max(a, b, c) in one v_max3_f32 (no canonicalisation of the operands).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
@@ -212,10 +223,32 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
+// s_waitcnt lgkmcnt(0) followed by empty asm statements that redefine each of
+// the given registers: every later use reads the post-wait value.
+template <typename T>
+__device__ __forceinline__ void redefine(T &r) {
+  asm volatile("" : "+v"(r));
+}
+template <typename... T>
+__device__ __forceinline__ void lds_wait_all(T &...regs) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  (redefine(regs), ...);
+}
+
 // s_waitcnt lgkmcnt(0), with the given registers routed through it so that
 // no use of them can be scheduled before the wait.
 __device__ __forceinline__ void lds_wait(u32x2 &a, u32x2 &b, u32x2 &c, u32x2 &d) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void lds_wait(u32x4 &a, u32x4 &b, u32x4 &c, u32x4 &d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void lds_wait(u32x4 &a, u32x4 &b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void lds_wait(u32x4 &a) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a)); }
+__device__ __forceinline__ void lds_wait(u32x2 &a, u32x2 &b, u32x4 &c) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c));
 }
 __device__ __forceinline__ void lds_wait(u32x2 &a, u32x2 &b) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
