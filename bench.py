@@ -19,8 +19,10 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,6 +36,32 @@ METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "fwd_encoder_b4h16n4096d128"
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_bwd_encoder_b4h16n4096d128_hbm_traffic.md")
+BWD_SOURCES = ["exact_io_aware_49_amd/csrc/fa_bwd_bf16.hip", "exact_io_aware_49_amd/csrc/fa_device.h"]
+
+
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per backward launch from the committed rocprofv3 counter summary,
+    or None if it is missing or the backward kernels changed since it was taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    tot = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not sha or not tot or sha.group(1) != sources_sha(BWD_SOURCES):
+        return None
+    return int(tot.group(1))
 
 
 def fwd_flops(B, H, N, d, causal):
@@ -166,8 +194,9 @@ def main(argv=None):
     else:
         dom = {"kernel": "fa_fwd_bf16_kernel", "flops": ff, "ms": fwd_ms}
     achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    traffic = measured_traffic() if dom["kernel"].startswith("fa_bwd") and w.name == DEFAULT_WORKLOAD else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom["kernel"],
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom["kernel"],
                 "avg_launch_ms": round(dom["ms"], 4)}
 
     line = {

@@ -143,8 +143,8 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
   const int l32 = lane & 31;
   const int nqb = (N + BR - 1) / BR;
   const int nbh = gridDim.x / nqb;
-  const int bh = blockIdx.x % nbh;
-  const int qb = CAUSAL ? (nqb - 1 - (int)blockIdx.x / nbh) : ((int)blockIdx.x / nbh);
+  int bh, qb;
+  map_block(blockIdx.x, nqb, nbh, CAUSAL, bh, qb);  // same-head blocks share an XCD's L2
   const size_t head_off = (size_t)bh * N * D;
   const int q0 = qb * BR;
   const int qw0 = q0 + 32 * wave;
@@ -273,8 +273,10 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
   const int l32 = lane & 31;
   const int nkb = (N + BKV - 1) / BKV;
   const int nbh = gridDim.x / nkb;
-  const int bh = blockIdx.x % nbh;
-  const int kblk = blockIdx.x / nbh;  // ascending: with a causal mask the first blocks have the most work
+  int bh, rb;
+  map_block(blockIdx.x, nkb, nbh, CAUSAL, bh, rb);  // same-head blocks share an XCD's L2
+  // with a causal mask the lowest key blocks have the most work: run them first
+  const int kblk = CAUSAL ? (nkb - 1 - rb) : rb;
   const size_t head_off = (size_t)bh * N * D;
   const int kb0 = kblk * BKV;
   const int kw0 = kb0 + 32 * wave;

@@ -111,6 +111,37 @@ __device__ __forceinline__ int swap_bits23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
+// Map the linear workgroup id to (batch*head, row block) for grids of
+// nbh * nqb workgroups.  Workgroups are
+// dispatched round-robin over the 8 XCDs; grouping consecutive ids of one XCD
+// onto the same heads keeps a head's K/V in that XCD's L2.  Causal launches
+// put the highest row blocks first (the heaviest for a query-block owner).
+__device__ __forceinline__ void map_block(int bid, int nqb, int nbh, bool causal, int &bh, int &qb) {
+  const int total = nqb * nbh;
+  int id = bid;
+  if ((total & 7) == 0) {
+    const int per_xcd = total >> 3;
+    id = (bid & 7) * per_xcd + (bid >> 3);
+  }
+  if (causal) {
+    const int per_xcd = ((total & 7) == 0) ? (total >> 3) : total;
+    const int base = (id / per_xcd) * per_xcd;
+    const int local = id - base;
+    if (per_xcd % nqb == 0) {
+      const int heads_here = per_xcd / nqb;
+      const int qrank = local / heads_here;
+      bh = base / nqb + (local % heads_here);
+      qb = nqb - 1 - qrank;
+      return;
+    }
+    bh = id / nqb;
+    qb = nqb - 1 - (id % nqb);
+    return;
+  }
+  bh = id / nqb;
+  qb = id % nqb;
+}
+
 // ---- staging of 4-row x 8-column bf16 blocks into LDS -----------------------
 // A block is rows r0..r0+3, columns 8g..8g+7 of a row-major [nrows][ld] bf16
 // matrix: four 16-byte vectors, one per row.  Rows >= nrows read as zero.

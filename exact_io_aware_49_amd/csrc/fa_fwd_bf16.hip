@@ -65,36 +65,6 @@ __device__ __forceinline__ int swz_v(int r) {
   return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// Map the linear workgroup id to (batch*head, query block).  Workgroups are
-// dispatched round-robin over the 8 XCDs; grouping consecutive ids of one XCD
-// onto the same heads keeps a head's K/V in that XCD's L2.  Causal launches
-// run the heaviest query blocks (most key tiles) first.
-__device__ __forceinline__ void map_block(int bid, int nqb, int nbh, bool causal, int &bh, int &qb) {
-  const int total = nqb * nbh;
-  int id = bid;
-  if ((total & 7) == 0) {
-    const int per_xcd = total >> 3;
-    id = (bid & 7) * per_xcd + (bid >> 3);
-  }
-  if (causal) {
-    const int per_xcd = ((total & 7) == 0) ? (total >> 3) : total;
-    const int base = (id / per_xcd) * per_xcd;
-    const int local = id - base;
-    if (per_xcd % nqb == 0) {
-      const int heads_here = per_xcd / nqb;
-      const int qrank = local / heads_here;
-      bh = base / nqb + (local % heads_here);
-      qb = nqb - 1 - qrank;
-      return;
-    }
-    bh = id / nqb;
-    qb = nqb - 1 - (id % nqb);
-    return;
-  }
-  bh = id / nqb;
-  qb = id % nqb;
-}
-
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
