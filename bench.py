@@ -190,7 +190,8 @@ def main(argv=None):
 
     # dominant by time: the backward launch (two kernels) or the forward kernel
     if bwd_ms >= fwd_ms:
-        dom = {"kernel": "fa_bwd (fa_bwd_dq_kernel + fa_bwd_dkdv_kernel)", "flops": bf, "ms": bwd_ms}
+        dkdv = "fa_bwd_dkdv_pair_kernel" if d == 128 else "fa_bwd_dkdv_kernel"
+        dom = {"kernel": f"fa_bwd (fa_bwd_dq_kernel + {dkdv})", "flops": bf, "ms": bwd_ms}
     else:
         dom = {"kernel": "fa_fwd_bf16_kernel", "flops": ff, "ms": fwd_ms}
     achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12

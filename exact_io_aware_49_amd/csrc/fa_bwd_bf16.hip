@@ -14,10 +14,18 @@
 //                         then streams K/V tiles of 64 keys:
 //                         S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
 //                         Lane = query row, so lse and D are per-lane scalars.
-//   fa_bwd_dkdv_kernel -- owns 128 keys (32 per wave), K and V rows held in
-//                         registers.  Streams Q/dO tiles of 64 queries:
+//   fa_bwd_dkdv_kernel -- (d = 64) owns 128 keys (32 per wave), K and V rows
+//                         held in registers.  Streams Q/dO tiles of 64 queries:
 //                         S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
 //                         Lane = key.
+//   fa_bwd_dkdv_pair_kernel -- (d = 128) the same work for 128 keys split over
+//                         8 waves in pairs that share a SIMD and a 32-key group:
+//                         one wave computes S, P and dV (K rows in registers),
+//                         its partner dP, dS and dK (V rows in registers), with
+//                         P passed through LDS.  One wave per key group would
+//                         need about 330 registers at d = 128 (one wave per
+//                         SIMD, nothing to hide its latencies); a pair needs
+//                         under 256 each, so two waves share every SIMD.
 // Streamed tiles go from HBM straight into LDS (buffer_load ... lds, double
 // buffered) as row-major tiles whose 16-byte chunks are XOR-permuted per row.
 // Each tile is read twice from that single copy: as rows (ds_read_b128, the A
@@ -45,13 +53,14 @@ struct BwdCfg {
 
 // One 64-row tile of a [N, D] head slab (rows r0 .. r0+63) into LDS at `dst`,
 // split over the 4 waves; rows past N read as zero.
-template <int D>
+template <int D, int NW = 4>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, int r0, int wave,
                                            int lane) {
   using C = BwdCfg<D>;
+  constexpr int LPW = C::TB / 1024 / NW;  // loads per wave
 #pragma unroll
-  for (int u = 0; u < C::LPW; ++u) {
-    const int row0 = (wave * C::LPW + u) * C::RPI;
+  for (int u = 0; u < LPW; ++u) {
+    const int row0 = (wave * LPW + u) * C::RPI;
     const int row = row0 + lane / C::CPR;
     const uint32_t g = (uint32_t)(r0 + row) * C::RB + 16u * ((lane % C::CPR) ^ swz_rt<D>(row));
     load_lds16(rs, dst + row0 * C::RB, g);
@@ -255,7 +264,7 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
 
 // ============================================================== dK/dV kernel
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, (D == 64) ? 2 : 1)
+__global__ void __launch_bounds__(256, 2)
 fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                    const __bf16 *__restrict__ dO, const float *__restrict__ Dsum, const float *__restrict__ Lse2,
                    __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N, float scale_log2e, float scale) {
@@ -394,6 +403,188 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
 }
 
 template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1)
+fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
+                   const __bf16 *__restrict__ dO, const float *__restrict__ Dsum, const float *__restrict__ Lse2,
+                   __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N, float scale_log2e, float scale) {
+  using C = BwdCfg<D>;
+  constexpr int TB = C::TB;
+  constexpr int RB = C::RB;
+  constexpr int BKV = 128;                  // keys per workgroup: 4 groups of 32
+  constexpr int STAGE = 2 * TB + 1024;      // Q tile, dO tile, lse*log2e[64], D[64]
+  constexpr int PBUF = 2 * STAGE;           // P exchange: [sub-tile 2][key group 4][half 2][2][64 lanes x 16 B]
+  __shared__ __align__(1024) unsigned char smem[2 * STAGE + 32768];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // waves w and w + 4 share a SIMD and a key group: role 0 (w < 4) forms P and
+  // accumulates dV, role 1 forms dS from the P of its partner and accumulates dK
+  const int role = wave >> 2;
+  const int kg = wave & 3;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int nkb = (N + BKV - 1) / BKV;
+  const int nbh = gridDim.x / nkb;
+  int bh, rb;
+  map_block(blockIdx.x, nkb, nbh, CAUSAL, bh, rb);  // same-head blocks share an XCD's L2
+  // with a causal mask the lowest key blocks have the most work: run them first
+  const int kblk = CAUSAL ? (nkb - 1 - rb) : rb;
+  const size_t head_off = (size_t)bh * N * D;
+  const int kb0 = kblk * BKV;
+  const int kw0 = kb0 + 32 * kg;
+  const int my_k = kw0 + l32;
+  const bool k_ok = my_k < N;
+
+  // B operand of the first products: K rows (role 0, S = Q K^T) or V rows (role 1, dP = dO V^T)
+  bf16x8 bf[C::KSTEPS];
+  {
+    const __bf16 *src = (role == 0) ? K : V;
+    const size_t roff = head_off + (size_t)(k_ok ? my_k : 0) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) bf[ks] = as_bf16x8(k_ok ? ld16(src + roff + 16 * ks) : u32x4{0, 0, 0, 0});
+  }
+
+  const int nqt = (N + 63) / 64;
+  const int qt0 = CAUSAL ? (kb0 / 64) : 0;
+
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(Lse2 + (size_t)bh * N, (uint32_t)N * 4u);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(Dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  TileOffsets<D> to;
+  to.init(lane, lds_addr(smem));  // transposed reads of the Q tile; the dO tile is TB further
+
+  auto issue = [&](int t, int stage) {
+    unsigned char *base = smem + stage * STAGE;
+    issue_tile<D, 8>(qrs, base, t * 64, wave, lane);
+    issue_tile<D, 8>(ors, base + TB, t * 64, wave, lane);
+    if (wave == 0) load_lds4(lrs, base + 2 * TB, (uint32_t)(t * 64 + lane) * 4u);
+    if (wave == 1) load_lds4(drs, base + 2 * TB + 256, (uint32_t)(t * 64 + lane) * 4u);
+  };
+
+  floatx16 acc[C::CT];  // dV^T (role 0) or dK^T (role 1), lane = key
+#pragma unroll
+  for (int ct = 0; ct < C::CT; ++ct) acc[ct] = floatx16{0};
+
+  auto step = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < nqt) issue(t + 1, BUF ^ 1);
+    const int qs = t * 64;
+    // every query of the tile is before this key group's keys: nothing to do,
+    // but the workgroup barrier below is still passed
+    const bool active = !(CAUSAL && qs + 63 < kw0);
+    const unsigned char *Qs = smem + BUF * STAGE;
+    const float *lst = reinterpret_cast<const float *>(Qs + 2 * TB);
+    const bool need_mask = (CAUSAL && qs < kw0 + 31) || (qs + 64 > N) || (kb0 + BKV > N);
+
+    // ---- first products for both 32-query sub-tiles: S (role 0) or dP (role 1)
+    floatx16 first[2];
+    if (active) {
+      const unsigned char *As = Qs + role * TB;  // Q rows or dO rows
+      static_for<2>([&](auto qtc) {
+        constexpr int QT = decltype(qtc)::value;
+        floatx16 a = floatx16{0};
+        bf16x8 r[C::KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) r[ks] = as_bf16x8(ld16(As + to.rows[ks] + 32 * QT * RB));
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) a = mfma32x32x16(r[ks], bf[ks], a);
+        first[QT] = a;
+      });
+    }
+    u32x4 pw[2][2];  // role 0: P of (sub-tile, half) as bf16, lane = key, 8 queries
+    if (role == 0 && active) {
+      static_for<2>([&](auto qtc) {
+        constexpr int QT = decltype(qtc)::value;
+        static_for<2>([&](auto mc) {
+          constexpr int M = decltype(mc)::value;
+          const int qoff = 32 * QT + 16 * M + 8 * half;  // tile-local query of register 8M
+          const floatx4 l0 = *reinterpret_cast<const floatx4 *>(lst + qoff);
+          const floatx4 l1 = *reinterpret_cast<const floatx4 *>(lst + qoff + 4);
+          float pf[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float p2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int j = 2 * i + e;
+              const float lq = (j < 4) ? l0[j] : l1[j - 4];
+              float p = fast_exp2(__builtin_fmaf(first[QT][8 * M + j], scale_log2e, -lq));
+              if (need_mask) {
+                const int q = qs + qoff + j;
+                if (q >= N || !k_ok || (CAUSAL && q < my_k)) p = 0.f;
+              }
+              p2[e] = p;
+              pf[j] = p;
+            }
+            pw[QT][M][i] = pack_bf16x2(p2[0], p2[1]);
+          }
+          // float32 P for the partner's dS, in two 16-byte halves
+          unsigned char *slot = smem + PBUF + ((QT * 4 + kg) * 2 + M) * 2048 + lane * 16;
+          *reinterpret_cast<floatx4 *>(slot) = floatx4{pf[0], pf[1], pf[2], pf[3]};
+          *reinterpret_cast<floatx4 *>(slot + 1024) = floatx4{pf[4], pf[5], pf[6], pf[7]};
+        });
+      });
+    }
+    __syncthreads();  // P of every key group is in LDS
+    if (!active) return;
+    if (role == 0) {
+      static_for<2>([&](auto qtc) {
+        constexpr int QT = decltype(qtc)::value;
+        static_for<2>([&](auto mc) {
+          constexpr int M = decltype(mc)::value;
+          constexpr int OFFQ = BUF * STAGE + 16 * (2 * QT + M) * RB;
+          mfma_transposed<D, OFFQ + TB>(acc, to, as_bf16x8(pw[QT][M]));  // dV^T += dO^T P
+        });
+      });
+    } else {
+      static_for<2>([&](auto qtc) {
+        constexpr int QT = decltype(qtc)::value;
+        static_for<2>([&](auto mc) {
+          constexpr int M = decltype(mc)::value;
+          const int qoff = 32 * QT + 16 * M + 8 * half;
+          const floatx4 d0 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff);
+          const floatx4 d1 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff + 4);
+          const unsigned char *slot = smem + PBUF + ((QT * 4 + kg) * 2 + M) * 2048 + lane * 16;
+          const floatx4 p0 = *reinterpret_cast<const floatx4 *>(slot);
+          const floatx4 p1 = *reinterpret_cast<const floatx4 *>(slot + 1024);
+          u32x4 sw;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float s2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int j = 2 * i + e;
+              const float dq = (j < 4) ? d0[j] : d1[j - 4];
+              const float p = (j < 4) ? p0[j] : p1[j - 4];
+              s2[e] = p * (first[QT][8 * M + j] - dq);
+            }
+            sw[i] = pack_bf16x2(s2[0], s2[1]);
+          }
+          constexpr int OFFQ = BUF * STAGE + 16 * (2 * QT + M) * RB;
+          mfma_transposed<D, OFFQ>(acc, to, as_bf16x8(sw));  // dK^T += Q^T dS
+        });
+      });
+    }
+  };
+
+  if (qt0 < nqt) issue(qt0, 0);
+  for (int t = qt0; t < nqt; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nqt) step(std::integral_constant<int, 1>{}, t + 1);
+  }
+
+  if (k_ok) {
+    if (role == 0) store_rows_bf16<D>(dV + head_off + (size_t)my_k * D, acc, 1.0f, half);
+    else store_rows_bf16<D>(dK + head_off + (size_t)my_k * D, acc, scale, half);
+  }
+}
+
+template <int D, bool CAUSAL>
 hipError_t launch(const void *q, const void *k, const void *v, const void *o, const void *dout,
                   const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int H, int N, float scale,
                   hipStream_t stream) {
@@ -409,9 +600,14 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
                      (const __bf16 *)dout, lse, (__bf16 *)dq, dsum, lse2, N, c, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, stream,
-                     (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
-                     (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, N, c, scale);
+  if constexpr (D == 64)
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, stream,
+                       (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
+                       (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, N, c, scale);
+  else
+    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(512), 0, stream,
+                       (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
+                       (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, N, c, scale);
   return hipGetLastError();
 }
 
