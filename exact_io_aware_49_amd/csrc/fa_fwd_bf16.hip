@@ -31,6 +31,10 @@
 //   * The running maximum only moves when a tile's maximum exceeds it by more
 //     than 2^8 in exp2 units; O and l share the reference, so O / l is
 //     unchanged and every P stays below 2^8.
+//   * A tile step runs in chunks of 16 keys; each chunk's LDS fragments (K
+//     rows for the next tile's scores, V^T rows for this tile's product) are
+//     read one chunk ahead into a second register set, so their latency runs
+//     under the previous chunk's matrix products.
 //   * Causal: tiles entirely above the diagonal are never loaded; a wave whose
 //     rows are all above a tile skips its math; only diagonal and ragged tiles
 //     pay for masking.
@@ -178,6 +182,42 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   constexpr int NCH = 2 * C::NKT;            // P chunks of 8 keys per lane per tile
   constexpr int QK_PER_CH = C::KSTEPS / 2;   // score MFMAs of the next tile per chunk
 
+  // LDS fragments of one chunk: K rows for QK_PER_CH score k-steps of the next
+  // tile and V^T rows for one 16-key slice of the current tile
+  struct Frag {
+    u32x4 k[QK_PER_CH];
+    u32x2 v[C::CT][2];
+  };
+  const uint32_t kbase = lds_addr(smem);
+  uint32_t kaddr[C::KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks) kaddr[ks] = kbase + koff[ks];
+  auto read_frag = [&](auto bufc, auto cc, Frag &f) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr int CH = decltype(cc)::value;
+    constexpr int first = CH * QK_PER_CH;
+    constexpr int kt = first / C::KSTEPS;
+    constexpr int k0 = first % C::KSTEPS;
+    constexpr int KOFF = (BUF ^ 1) * TB + 32 * kt * RB;   // K buffer of tile t+1
+    constexpr int VOFF = BUF * TB + (16 * CH) * RB;       // V buffer of tile t, rows 16 CH..
+#pragma unroll
+    for (int i = 0; i < QK_PER_CH; ++i) f.k[i] = ds_read_b128_at<KOFF>(kaddr[k0 + i]);
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+      f.v[ct][0] = ds_read_tr16_at<VOFF>(voff[ct][0]);
+      f.v[ct][1] = ds_read_tr16_at<VOFF>(voff[ct][1]);
+    }
+  };
+  auto frag_wait = [&](Frag &f) {
+    static_assert(QK_PER_CH == 4 || QK_PER_CH == 2, "fragment sizes");
+    static_assert(C::CT == 4 || C::CT == 2, "fragment sizes");
+    if constexpr (QK_PER_CH == 4 && C::CT == 4)
+      lds_wait_all(f.k[0], f.k[1], f.k[2], f.k[3], f.v[0][0], f.v[0][1], f.v[1][0], f.v[1][1], f.v[2][0],
+                   f.v[2][1], f.v[3][0], f.v[3][1]);
+    else
+      lds_wait_all(f.k[0], f.k[1], f.v[0][0], f.v[0][1], f.v[1][0], f.v[1][1]);
+  };
+
   // One tile step.  BUF is the V buffer of tile t (and the K buffer of tile t).
   auto step = [&](auto bufc, int t, floatx16 (&cur)[C::NKT], floatx16 (&nxt)[C::NKT]) {
     constexpr int BUF = decltype(bufc)::value;
@@ -188,9 +228,9 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 
     const int kb = t * C::BC;
     const bool act = !CAUSAL || (kb <= qw0 + 31);
-    const bool act_n = (t + 1 < ntiles) && (!CAUSAL || (kb + C::BC <= qw0 + 31));
-    const unsigned char *knext = smem + (BUF ^ 1) * TB;
 
+    Frag fa, fb;
+    if (act) read_frag(bufc, std::integral_constant<int, 0>{}, fa);
     float mc = 0.f;
     if (act) {
       // ---- masking (diagonal and ragged tiles only)
@@ -229,7 +269,10 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
       mc = (m_ref == -INFINITY) ? 0.f : m_ref * scale_log2e;
     }
 
-    // ---- P of tile t, O^T += V^T P^T, interleaved with S^T of tile t+1
+    // ---- P of tile t, O^T += V^T P^T, interleaved with S^T of tile t+1.
+    // Chunk CH covers keys [16 CH, 16 CH + 16) of tile t (8 per lane) and
+    // score k-steps [CH QK_PER_CH, +QK_PER_CH) of tile t+1.  Its LDS fragments
+    // are read one chunk ahead, into the other of two register sets.
     auto chunk_p = [&](int kt, int m) -> bf16x8 {
       u32x4 pw;
 #pragma unroll
@@ -241,39 +284,27 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
       }
       return as_bf16x8(pw);
     };
-    auto chunk_pv = [&](auto cc, const bf16x8 &pb) {
-      constexpr int CH = decltype(cc)::value;
-      constexpr int ROWOFF = BUF * TB + (16 * CH) * RB;  // kt = CH/2, m = CH%2: row 32kt + 16m = 16*CH
-#pragma unroll
-      for (int c2 = 0; c2 < C::CT; c2 += 2) {
-        u32x2 l0 = ds_read_tr16_at<ROWOFF>(voff[c2][0]);
-        u32x2 h0 = ds_read_tr16_at<ROWOFF>(voff[c2][1]);
-        u32x2 l1 = ds_read_tr16_at<ROWOFF>(voff[c2 + 1][0]);
-        u32x2 h1 = ds_read_tr16_at<ROWOFF>(voff[c2 + 1][1]);
-        lds_wait(l0, h0, l1, h1);
-        const u32x4 a0 = {l0[0], l0[1], h0[0], h0[1]};
-        const u32x4 a1 = {l1[0], l1[1], h1[0], h1[1]};
-        oacc[c2] = mfma32x32x16(as_bf16x8(a0), pb, oacc[c2]);
-        oacc[c2 + 1] = mfma32x32x16(as_bf16x8(a1), pb, oacc[c2 + 1]);
-      }
-    };
-    auto chunk_qk = [&](int ch) {
-      // score MFMAs [ch * QK_PER_CH, +QK_PER_CH) of tile t+1, kt-major
-      const int first = ch * QK_PER_CH;
-      const int kt = first / C::KSTEPS;
-      const int k0 = first % C::KSTEPS;
-      if (k0 == 0) nxt[kt] = floatx16{0};
-      qk_steps(nxt[kt], knext, kt, k0, QK_PER_CH);
-    };
-
     // (a wave that is active for tile t but not for t+1 -- the last tile, or
     // the causal diagonal -- computes scores it will not use; they are discarded)
     if (act) {
       static_for<NCH>([&](auto cc) {
         constexpr int CH = decltype(cc)::value;
+        Frag &f = (CH % 2 == 0) ? fa : fb;
+        Frag &g = (CH % 2 == 0) ? fb : fa;
         const bf16x8 pb = chunk_p(CH / 2, CH % 2);
-        chunk_qk(CH);
-        chunk_pv(cc, pb);
+        frag_wait(f);
+        if constexpr (CH + 1 < NCH) read_frag(bufc, std::integral_constant<int, CH + 1>{}, g);
+        constexpr int first = CH * QK_PER_CH;
+        constexpr int kt = first / C::KSTEPS;
+        constexpr int k0 = first % C::KSTEPS;
+        if constexpr (k0 == 0) nxt[kt] = floatx16{0};
+#pragma unroll
+        for (int i = 0; i < QK_PER_CH; ++i) nxt[kt] = mfma32x32x16(as_bf16x8(f.k[i]), qf[k0 + i], nxt[kt]);
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) {
+          const u32x4 av = {f.v[ct][0][0], f.v[ct][0][1], f.v[ct][1][0], f.v[ct][1][1]};
+          oacc[ct] = mfma32x32x16(as_bf16x8(av), pb, oacc[ct]);
+        }
       });
     }
   };
