@@ -100,6 +100,31 @@ def gen_qkv(shape, dtype: str, seed: int, with_do: bool = False):
     return gen_tensors(shape, dtype, seed, 4 if with_do else 3)
 
 
+def gen_gqa(B: int, hq: int, hkv: int, N: int, d: int, dtype: str, seed: int, with_do: bool = False):
+    """Q [B,hq,N,d], K and V [B,hkv,N,d] (and dO [B,hq,N,d]), drawn in that order.
+
+    The inputs of attention with hq query heads sharing hkv key/value heads.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shapes = [(B, hq, N, d), (B, hkv, N, d), (B, hkv, N, d)] + ([(B, hq, N, d)] if with_do else [])
+    out = []
+    for shp in shapes:
+        a = rng.standard_normal(size=shp, dtype=np.float32)
+        if dtype == "bf16":
+            a = bf16_round(a)
+        out.append(a)
+    return out
+
+
+# Shared K/V head shapes used by the parity tests: a grouped-query layout with
+# 8 query heads per K/V head (32 query heads of 128 over 4 K/V heads, 2K tokens)
+# and multi-query attention (one K/V head).
+GQA_CASES = {
+    "gqa_causal_b2hq32hkv4n2048d128": dict(B=2, hq=32, hkv=4, N=2048, d=128, causal=True, seed=31),
+    "mqa_b2hq16hkv1n1024d64": dict(B=2, hq=16, hkv=1, N=1024, d=64, causal=False, seed=32),
+}
+
+
 def workload_inputs(w: Workload):
     """Inputs of a named workload: Q, K, V (and dO for a backward workload)."""
     return gen_qkv(w.shape, w.dtype, w.seed, with_do=(w.kind == "bwd"))

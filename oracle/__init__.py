@@ -29,4 +29,6 @@ from .attention import (  # noqa: F401
     attention_probs,
     attention_backward,
     attention_backward_from_probs,
+    kv_head,
+    group_sum,
 )

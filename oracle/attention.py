@@ -35,7 +35,17 @@ are upcast, never rounded further).  Work is done one (batch, head) pair at a
 time; the row-chunked forward keeps whole rows of S (every key), so it is the
 same arithmetic with bounded memory.
 
-Layout: q, k, v, dO are [B, H, N, d]; lse is [B, H, N].
+Multi-query attention (named as a FlashAttention-2 capability in
+"FlashAttention (DE)", section "Evolution und Weiterentwicklungen") lets
+several query heads share one key/value head.  The pages give no definition;
+the reading used here is contiguous groups: with Hq query heads and Hkv K/V
+heads (Hkv divides Hq), query head h reads K/V head h // (Hq / Hkv).  Hkv = 1
+is multi-query attention and Hkv = Hq ordinary multi-head attention.  Each
+query head's output is the attention equation above with its group's K and V;
+a shared K/V head's gradient is the sum of the gradients over the query heads
+that read it (the chain rule for a shared input).
+
+Layout: q, dO are [B, Hq, N, d]; k, v are [B, Hkv, N, d]; lse is [B, Hq, N].
 """
 
 from __future__ import annotations
@@ -95,6 +105,31 @@ def _lse(m: np.ndarray, l: np.ndarray) -> np.ndarray:
     return out
 
 
+def kv_head(h: int, hq: int, hkv: int) -> int:
+    """The K/V head read by query head h when hq query heads share hkv K/V heads.
+
+    Contiguous groups of hq / hkv query heads per K/V head (reading of the
+    multi-query attention named in "FlashAttention (DE)", section
+    "Evolution und Weiterentwicklungen").
+    """
+    if hkv < 1 or hq % hkv != 0:
+        raise ValueError(f"{hq} query heads cannot share {hkv} K/V heads")
+    return h // (hq // hkv)
+
+
+def group_sum(g, hkv: int) -> np.ndarray:
+    """Sum per-query-head gradients [B, Hq, N, d] over each K/V head's group -> [B, Hkv, N, d].
+
+    A K/V head read by several query heads receives the sum of their
+    gradients (chain rule for a shared input).
+    """
+    g = np.asarray(g, dtype=np.float64)
+    B, hq, n, d = g.shape
+    if hkv < 1 or hq % hkv != 0:
+        raise ValueError(f"{hq} query heads cannot share {hkv} K/V heads")
+    return g.reshape(B, hkv, hq // hkv, n, d).sum(axis=2)
+
+
 def _head_forward(q, k, v, causal: bool, scale: float, row_ids):
     s = scores(q, k, scale)
     if causal:
@@ -105,7 +140,7 @@ def _head_forward(q, k, v, causal: bool, scale: float, row_ids):
 
 
 def attention_forward(q, k, v, causal: bool, scale: float, row_chunk: int | None = None):
-    """Exact attention forward.  q, k, v: [B, H, N, d] -> (O [B,H,N,d], lse [B,H,N]), float64.
+    """Exact attention forward.  q: [B, Hq, N, d], k, v: [B, Hkv, N, d] -> (O [B,Hq,N,d], lse [B,Hq,N]).
 
     With `row_chunk`, query rows are processed `row_chunk` at a time; each
     chunk still sees every key, so the result is the same definition.
@@ -114,7 +149,8 @@ def attention_forward(q, k, v, causal: bool, scale: float, row_chunk: int | None
     k = np.asarray(k)
     v = np.asarray(v)
     B, H, N, d = q.shape
-    if k.shape != (B, H, k.shape[2], d) or v.shape[:3] != k.shape[:3]:
+    hkv = k.shape[1]
+    if k.shape != (B, hkv, k.shape[2], d) or v.shape[:3] != k.shape[:3] or hkv < 1 or H % hkv != 0:
         raise ValueError("q, k, v shapes do not match")
     o = np.empty((B, H, N, v.shape[3]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
@@ -124,8 +160,9 @@ def attention_forward(q, k, v, causal: bool, scale: float, row_chunk: int | None
             for r0 in range(0, N, step):
                 r1 = min(N, r0 + step)
                 rows = np.arange(r0, r1)
+                hk = kv_head(h, H, hkv)
                 o[b, h, r0:r1], lse[b, h, r0:r1] = _head_forward(
-                    q[b, h, r0:r1], k[b, h], v[b, h], causal, scale, rows)
+                    q[b, h, r0:r1], k[b, hk], v[b, hk], causal, scale, rows)
     return o, lse
 
 
@@ -137,8 +174,10 @@ def attention_forward_rows(q, k, v, causal: bool, scale: float, b: int, h: int, 
     where the full matrix would not fit in host memory).
     """
     rows = np.asarray(rows, dtype=np.int64)
-    return _head_forward(np.asarray(q)[b, h][rows], np.asarray(k)[b, h],
-                         np.asarray(v)[b, h], causal, scale, rows)
+    q = np.asarray(q)
+    k = np.asarray(k)
+    hk = kv_head(h, q.shape[1], k.shape[1])
+    return _head_forward(q[b, h][rows], k[b, hk], np.asarray(v)[b, hk], causal, scale, rows)
 
 
 def attention_probs(q, k, causal: bool, scale: float) -> np.ndarray:
@@ -149,7 +188,7 @@ def attention_probs(q, k, causal: bool, scale: float) -> np.ndarray:
     p = np.empty((B, H, N, k.shape[2]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            s = scores(q[b, h], k[b, h], scale)
+            s = scores(q[b, h], k[b, kv_head(h, H, k.shape[1])], scale)
             if causal:
                 s = causal_mask(s, np.arange(N))
             p[b, h] = softmax_rows(s)[0]
@@ -177,25 +216,28 @@ def attention_backward_from_probs(p, q, k, v, do, scale: float):
 
 
 def attention_backward(q, k, v, do, causal: bool, scale: float):
-    """Exact attention backward: -> (dQ, dK, dV), each [B, H, N, d] float64.
+    """Exact attention backward: -> (dQ [B,Hq,N,d], dK [B,Hkv,N,d], dV [B,Hkv,N,d]) float64.
 
-    P is formed from its definition (full S, two-pass softmax) for each head;
-    nothing from a forward pass on the GPU is used.
+    P is formed from its definition (full S, two-pass softmax) for each query
+    head; nothing from a forward pass on the GPU is used.  Per-query-head dK
+    and dV are summed over each K/V head's group.
     """
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
     do = np.asarray(do)
     B, H, N, d = q.shape
+    hkv = k.shape[1]
     dq = np.empty((B, H, N, d), dtype=np.float64)
     dk = np.empty((B, H, k.shape[2], d), dtype=np.float64)
     dv = np.empty((B, H, k.shape[2], v.shape[3]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            s = scores(q[b, h], k[b, h], scale)
+            hk = kv_head(h, H, hkv)
+            s = scores(q[b, h], k[b, hk], scale)
             if causal:
                 s = causal_mask(s, np.arange(N))
             p = softmax_rows(s)[0]
             dq[b, h], dk[b, h], dv[b, h] = attention_backward_from_probs(
-                p, q[b, h], k[b, h], v[b, h], do[b, h], scale)
-    return dq, dk, dv
+                p, q[b, h], k[b, hk], v[b, hk], do[b, h], scale)
+    return dq, group_sum(dk, hkv), group_sum(dv, hkv)

@@ -267,6 +267,66 @@ def pin_finite_differences():
     return out
 
 
+# --------------------------------------------------------------------------- shared K/V heads
+
+def _gqa_cases():
+    # (Hq, Hkv): multi-query, two groups, plain multi-head
+    return ((3, 1), (4, 2), (2, 2))
+
+
+def pin_gqa_brute_force():
+    """Query head h of Hq attends with K/V head floor(h * Hkv / Hq) (contiguous groups);
+    checked head by head against the pure-Python forward."""
+    out = []
+    r = _rng(21)
+    for (hq, hkv), n, causal in itertools.product(_gqa_cases(), (1, 4, 7), (False, True)):
+        d = 3
+        q = r.standard_normal((1, hq, n, d))
+        k, v = (r.standard_normal((1, hkv, n, d)) for _ in range(2))
+        o, lse = A.attention_forward(q, k, v, causal, 0.7)
+        for h in range(hq):
+            g = (h * hkv) // hq
+            bo, bl = brute_forward(q[0, h].tolist(), k[0, g].tolist(), v[0, g].tolist(), causal, 0.7)
+            err = max(_maxdiff(o[0, h], bo), _maxdiff(lse[0, h], bl))
+            _fail_if(not err <= 1e-14, f"shared K/V brute force Hq={hq} Hkv={hkv} n={n} h={h}: {err:.3e}", out)
+    return out
+
+
+def pin_gqa_finite_differences():
+    """Central differences of L = sum over query heads of sum(dO * O) with respect to the
+    shared K and V entries, through the pure-Python forward."""
+    out = []
+    r = _rng(22)
+    h = 1e-6
+    for (hq, hkv), causal in itertools.product(((3, 1), (4, 2)), (False, True)):
+        n, d, s = 4, 2, 0.8
+        q, do = (r.standard_normal((1, hq, n, d)) for _ in range(2))
+        k, v = (r.standard_normal((1, hkv, n, d)) for _ in range(2))
+
+        def loss(kk, vv):
+            tot = []
+            for qh in range(hq):
+                g = (qh * hkv) // hq
+                o, _ = brute_forward(q[0, qh].tolist(), kk[0, g].tolist(), vv[0, g].tolist(), causal, s)
+                tot += [o[i][c] * do[0, qh, i, c] for i in range(n) for c in range(d)]
+            return math.fsum(tot)
+
+        _, dk, dv = A.attention_backward(q, k, v, do, causal, s)
+        for name, x, gr in (("dK", k, dk), ("dV", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp = x.copy()
+                xm = x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                num[idx] = ((loss(xp, v) - loss(xm, v)) if name == "dK" else (loss(k, xp) - loss(k, xm))) / (2 * h)
+            scale_ref = max(1.0, float(np.abs(num).max()))
+            err = float(np.abs(num - np.asarray(gr)).max()) / scale_ref if np.shape(gr) == x.shape else float("inf")
+            _fail_if(not err <= 1e-6, f"shared K/V finite differences {name} Hq={hq} Hkv={hkv} "
+                                      f"causal={causal}: rel {err:.3e}", out)
+    return out
+
+
 # --------------------------------------------------------------------------- library routines
 
 def pin_torch_float64():
@@ -349,6 +409,8 @@ ALL_PINS = [
     pin_torch_float64,
     pin_gradient_identities,
     pin_row_chunking,
+    pin_gqa_brute_force,
+    pin_gqa_finite_differences,
 ]
 
 

@@ -2,7 +2,9 @@
 
 A pin battery that passes on a wrong oracle proves nothing, so every mutant
 below -- a dropped scale, a transposed operand, a sign error, an off-by-one
-mask, a missing log, a dropped gradient term -- must make at least one pin fail.
+mask, a missing log, a dropped gradient term, a wrong query-head to K/V-head
+mapping, a missing sum over a shared K/V head's group -- must make at least
+one pin fail.
 """
 
 import numpy as np
@@ -93,6 +95,24 @@ def m_bwd_dv_untransposed(p, q, k, v, do, scale):
     return dq, dk, np.asarray(p, np.float64) @ np.asarray(do, np.float64)
 
 
+def m_kv_head_modulo(h, hq, hkv):
+    if hkv < 1 or hq % hkv != 0:
+        raise ValueError("bad grouping")
+    return h % hkv  # interleaved instead of contiguous groups
+
+
+def m_group_first(g, hkv):
+    g = np.asarray(g, np.float64)
+    B, hq, n, d = g.shape
+    return g.reshape(B, hkv, hq // hkv, n, d)[:, :, 0]  # first head of the group only
+
+
+def m_group_mean(g, hkv):
+    g = np.asarray(g, np.float64)
+    B, hq, n, d = g.shape
+    return g.reshape(B, hkv, hq // hkv, n, d).mean(axis=2)
+
+
 MUTANTS = [
     ("scores", m_no_scale),
     ("scores", m_transposed_scores),
@@ -107,6 +127,9 @@ MUTANTS = [
     ("attention_backward_from_probs", m_bwd_no_transpose_dk),
     ("attention_backward_from_probs", m_bwd_no_scale_dq),
     ("attention_backward_from_probs", m_bwd_dv_untransposed),
+    ("kv_head", m_kv_head_modulo),
+    ("group_sum", m_group_first),
+    ("group_sum", m_group_mean),
 ]
 
 
