@@ -10,8 +10,11 @@ from .fa import (  # noqa: F401
     backward,
     default_scale,
     fa_bwd,
+    fa_bwd_gqa,
+    fa_bwd_gqa_workspace_size,
     fa_bwd_workspace_size,
     fa_fwd,
+    fa_fwd_gqa,
     fa_status_string,
     fa_version,
     forward,

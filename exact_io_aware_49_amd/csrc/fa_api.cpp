@@ -35,6 +35,12 @@ int check_common(int B, int H, int N, int d, int causal, float scale, int dtype)
   return FA_OK;
 }
 
+// Hq query heads over Hkv >= 1 K/V heads in contiguous groups
+int check_heads(int Hq, int Hkv) {
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return FA_ERR_BAD_SHAPE;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -45,7 +51,7 @@ const char *fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a required pointer is NULL";
-    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H and N must be >= 1 and the tensor size must fit";
+    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H and N must be >= 1, the tensor size must fit, and the query heads must split evenly over the K/V heads";
     case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM: head dim d must be 64 or 128";
     case FA_ERR_UNSUPPORTED_DTYPE: return "FA_ERR_UNSUPPORTED_DTYPE: dtype not supported by this entry point";
     case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite and > 0";
@@ -57,43 +63,70 @@ const char *fa_status_string(int status) {
   }
 }
 
-int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
-           int causal, float scale, int dtype, void *stream) {
+int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int N,
+               int d, int causal, float scale, int dtype, void *stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
-  int st = check_common(B, H, N, d, causal, scale, dtype);
+  int st = check_common(B, Hq, N, d, causal, scale, dtype);
+  if (st == FA_OK) st = check_heads(Hq, Hkv);
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_MISALIGNED;
+  const int group = Hq / Hkv;
   hipError_t e;
   if (dtype == FA_DTYPE_BF16)
-    e = fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal == 1, scale, (hipStream_t)stream);
+    e = fa::launch_fwd_bf16(q, k, v, o, lse, B, Hq, group, N, d, causal == 1, scale, (hipStream_t)stream);
   else
-    e = fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, causal == 1, scale, (hipStream_t)stream);
+    e = fa::launch_fwd_f32(q, k, v, o, lse, B, Hq, group, N, d, causal == 1, scale, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
-  if (check_common(B, H, N, d, 0, 1.0f, dtype) != FA_OK || dtype != FA_DTYPE_BF16) return 0;
-  // D_i and lse_i * log2(e), one float32 each per query row
-  const size_t bytes = 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
+           int causal, float scale, int dtype, void *stream) {
+  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
+}
+
+size_t fa_bwd_gqa_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype) {
+  if (check_common(B, Hq, N, d, 0, 1.0f, dtype) != FA_OK || check_heads(Hq, Hkv) != FA_OK ||
+      dtype != FA_DTYPE_BF16)
+    return 0;
+  // D_i and lse_i * log2(e), one float32 each per query row; with the query
+  // heads of a group split over several workgroups, float32 partial dK and dV
+  // per split
+  const long long nqh = (long long)B * Hq;
+  const long long nkvh = (long long)B * Hkv;
+  size_t bytes = fa::bwd_partial_offset_floats(nqh, N) * sizeof(float);
+  const int nsplit = fa::bwd_splits(nkvh, N, Hq / Hkv);
+  if (nsplit > 1) bytes += 2 * (size_t)nsplit * (size_t)nkvh * (size_t)N * (size_t)d * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
+  return fa_bwd_gqa_workspace_size(B, H, H, N, d, dtype);
+}
+
+int fa_bwd_gqa(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+               void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+               int N, int d, int causal, float scale, int dtype, void *stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
+  int st = check_common(B, Hq, N, d, causal, scale, dtype);
+  if (st == FA_OK) st = check_heads(Hq, Hkv);
+  if (st != FA_OK) return st;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+  const size_t need = fa_bwd_gqa_workspace_size(B, Hq, Hkv, N, d, dtype);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_MISALIGNED;
+  hipError_t e = fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, (float *)workspace, B, Hq, Hq / Hkv, N,
+                                     d, causal == 1, scale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
            void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes, int B, int H, int N, int d,
            int causal, float scale, int dtype, void *stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
-  int st = check_common(B, H, N, d, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
-  const size_t need = fa_bwd_workspace_size(B, H, N, d, dtype);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
-    return FA_ERR_MISALIGNED;
-  hipError_t e = fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, (float *)workspace, B, H, N, d,
-                                     causal == 1, scale, (hipStream_t)stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d, causal, scale,
+                    dtype, stream);
 }
 
 }  // extern "C"

@@ -115,6 +115,21 @@ __device__ __forceinline__ void mfma_transposed(floatx16 (&acc)[D / 32], const T
   }
 }
 
+// Store a [32 rows x D] fp32 accumulator as float32 times `mul` (same register
+// layout as store_rows_bf16 below).
+template <int D>
+__device__ __forceinline__ void store_rows_f32(float *row, const floatx16 (&acc)[D / 32], float mul, int half) {
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const floatx4 w = {acc[ct][4 * g + 0] * mul, acc[ct][4 * g + 1] * mul, acc[ct][4 * g + 2] * mul,
+                         acc[ct][4 * g + 3] * mul};
+      *reinterpret_cast<floatx4 *>(row + 32 * ct + 8 * g + 4 * half) = w;
+    }
+  }
+}
+
 // Store a [32 rows x D] fp32 accumulator (lane = row l32, register r of column
 // tile ct = column 32*ct + 8*(r/4) + 4*half + r%4) as bf16 times `mul`.
 template <int D>
@@ -137,7 +152,7 @@ __global__ void __launch_bounds__(256, 2)
 fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                  const __bf16 *__restrict__ Og, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
                  __bf16 *__restrict__ dQ, float *__restrict__ Dsum, float *__restrict__ Lse2, int N,
-                 float scale_log2e, float scale) {
+                 int group, float scale_log2e, float scale) {
   using C = BwdCfg<D>;
   constexpr int TB = C::TB;
   constexpr int RB = C::RB;
@@ -191,8 +206,9 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
   if (CAUSAL) ntiles = min(ntiles, (min(q0 + BR, N) - 1) / 64 + 1);
 
   const uint32_t head_bytes = (uint32_t)N * RB;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + head_off, head_bytes);
+  const size_t kv_off = (size_t)(bh / group) * N * D;  // the K/V head this query head reads
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, head_bytes);
   TileOffsets<D> to;
   to.init(lane, lds_addr(smem));  // transposed reads are of the K tiles
 
@@ -264,10 +280,11 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
 
 // ============================================================== dK/dV kernel
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, 3)
 fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                    const __bf16 *__restrict__ dO, const float *__restrict__ Dsum, const float *__restrict__ Lse2,
-                   __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N, float scale_log2e, float scale) {
+                   __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, float *__restrict__ part, int N, int group,
+                   int nsplit, float scale_log2e, float scale) {
   using C = BwdCfg<D>;
   constexpr int TB = C::TB;
   constexpr int RB = C::RB;
@@ -281,11 +298,16 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int nkb = (N + BKV - 1) / BKV;
-  const int nbh = gridDim.x / nkb;
-  int bh, rb;
-  map_block(blockIdx.x, nkb, nbh, CAUSAL, bh, rb);  // same-head blocks share an XCD's L2
+  const int nkvh = gridDim.x / (nkb * nsplit);  // K/V heads
+  int vh, rb;
+  map_block(blockIdx.x, nkb, nkvh * nsplit, CAUSAL, vh, rb);  // same-head blocks share an XCD's L2
+  // the query heads of a K/V head's group may be split over nsplit workgroups,
+  // each writing a float32 partial dK/dV that a reduction kernel sums
+  const int bh = vh / nsplit;
+  const int split = vh - bh * nsplit;
   // with a causal mask the lowest key blocks have the most work: run them first
   const int kblk = CAUSAL ? (nkb - 1 - rb) : rb;
+  // bh is a K/V head; query heads bh * group .. bh * group + group - 1 read it
   const size_t head_off = (size_t)bh * N * D;
   const int kb0 = kblk * BKV;
   const int kw0 = kb0 + 32 * wave;
@@ -307,10 +329,10 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
   const int qt0 = CAUSAL ? (kb0 / 64) : 0;
 
   const uint32_t head_bytes = (uint32_t)N * RB;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(Lse2 + (size_t)bh * N, (uint32_t)N * 4u);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(Dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  // query heads g0 .. g1-1 of the group are this workgroup's share
+  const int g0 = (int)((long long)split * group / nsplit);
+  const int g1 = (int)((long long)(split + 1) * group / nsplit);
+  __amdgpu_buffer_rsrc_t qrs, ors, lrs, drs;  // the current query head's Q, dO, lse*log2e, D
   TileOffsets<D> to;
   to.init(lane, lds_addr(smem));  // transposed reads of the Q tile; the dO tile is TB further
 
@@ -390,15 +412,30 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
     });
   };
 
-  if (qt0 < nqt) issue(qt0, 0);
-  for (int t = qt0; t < nqt; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < nqt) step(std::integral_constant<int, 1>{}, t + 1);
+  for (int g = g0; g < g1; ++g) {
+    const size_t hq = (size_t)bh * group + g;  // query head
+    qrs = make_rsrc(Q + hq * N * D, head_bytes);
+    ors = make_rsrc(dO + hq * N * D, head_bytes);
+    lrs = make_rsrc(Lse2 + hq * N, (uint32_t)N * 4u);
+    drs = make_rsrc(Dsum + hq * N, (uint32_t)N * 4u);
+    if (g > g0) __syncthreads();  // every wave is done with the previous head's tiles
+    issue(qt0, 0);
+    for (int t = qt0; t < nqt; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < nqt) step(std::integral_constant<int, 1>{}, t + 1);
+    }
   }
 
   if (k_ok) {
-    store_rows_bf16<D>(dK + head_off + (size_t)my_k * D, dkacc, scale, half);
-    store_rows_bf16<D>(dV + head_off + (size_t)my_k * D, dvacc, 1.0f, half);
+    if (nsplit == 1) {
+      store_rows_bf16<D>(dK + head_off + (size_t)my_k * D, dkacc, scale, half);
+      store_rows_bf16<D>(dV + head_off + (size_t)my_k * D, dvacc, 1.0f, half);
+    } else {  // partials [2][nsplit][K/V heads][N][D]: dK (scaled) then dV
+      const size_t per = (size_t)nkvh * N * D;
+      const size_t off = (size_t)split * per + head_off + (size_t)my_k * D;
+      store_rows_f32<D>(part + off, dkacc, scale, half);
+      store_rows_f32<D>(part + (size_t)nsplit * per + off, dvacc, 1.0f, half);
+    }
   }
 }
 
@@ -406,7 +443,8 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 1)
 fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                    const __bf16 *__restrict__ dO, const float *__restrict__ Dsum, const float *__restrict__ Lse2,
-                   __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int N, float scale_log2e, float scale) {
+                   __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, float *__restrict__ part, int N, int group,
+                   int nsplit, float scale_log2e, float scale) {
   using C = BwdCfg<D>;
   constexpr int TB = C::TB;
   constexpr int RB = C::RB;
@@ -425,11 +463,16 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int nkb = (N + BKV - 1) / BKV;
-  const int nbh = gridDim.x / nkb;
-  int bh, rb;
-  map_block(blockIdx.x, nkb, nbh, CAUSAL, bh, rb);  // same-head blocks share an XCD's L2
+  const int nkvh = gridDim.x / (nkb * nsplit);  // K/V heads
+  int vh, rb;
+  map_block(blockIdx.x, nkb, nkvh * nsplit, CAUSAL, vh, rb);  // same-head blocks share an XCD's L2
+  // the query heads of a K/V head's group may be split over nsplit workgroups,
+  // each writing a float32 partial dK/dV that a reduction kernel sums
+  const int bh = vh / nsplit;
+  const int split = vh - bh * nsplit;
   // with a causal mask the lowest key blocks have the most work: run them first
   const int kblk = CAUSAL ? (nkb - 1 - rb) : rb;
+  // bh is a K/V head; query heads bh * group .. bh * group + group - 1 read it
   const size_t head_off = (size_t)bh * N * D;
   const int kb0 = kblk * BKV;
   const int kw0 = kb0 + 32 * kg;
@@ -449,10 +492,10 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
   const int qt0 = CAUSAL ? (kb0 / 64) : 0;
 
   const uint32_t head_bytes = (uint32_t)N * RB;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(dO + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(Lse2 + (size_t)bh * N, (uint32_t)N * 4u);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(Dsum + (size_t)bh * N, (uint32_t)N * 4u);
+  // query heads g0 .. g1-1 of the group are this workgroup's share
+  const int g0 = (int)((long long)split * group / nsplit);
+  const int g1 = (int)((long long)(split + 1) * group / nsplit);
+  __amdgpu_buffer_rsrc_t qrs, ors, lrs, drs;  // the current query head's Q, dO, lse*log2e, D
   TileOffsets<D> to;
   to.init(lane, lds_addr(smem));  // transposed reads of the Q tile; the dO tile is TB further
 
@@ -572,55 +615,105 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
     }
   };
 
-  if (qt0 < nqt) issue(qt0, 0);
-  for (int t = qt0; t < nqt; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < nqt) step(std::integral_constant<int, 1>{}, t + 1);
+  for (int g = g0; g < g1; ++g) {
+    const size_t hq = (size_t)bh * group + g;  // query head
+    qrs = make_rsrc(Q + hq * N * D, head_bytes);
+    ors = make_rsrc(dO + hq * N * D, head_bytes);
+    lrs = make_rsrc(Lse2 + hq * N, (uint32_t)N * 4u);
+    drs = make_rsrc(Dsum + hq * N, (uint32_t)N * 4u);
+    if (g > g0) __syncthreads();  // every wave is done with the previous head's tiles
+    issue(qt0, 0);
+    for (int t = qt0; t < nqt; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < nqt) step(std::integral_constant<int, 1>{}, t + 1);
+    }
   }
 
   if (k_ok) {
-    if (role == 0) store_rows_bf16<D>(dV + head_off + (size_t)my_k * D, acc, 1.0f, half);
-    else store_rows_bf16<D>(dK + head_off + (size_t)my_k * D, acc, scale, half);
+    if (nsplit == 1) {
+      if (role == 0) store_rows_bf16<D>(dV + head_off + (size_t)my_k * D, acc, 1.0f, half);
+      else store_rows_bf16<D>(dK + head_off + (size_t)my_k * D, acc, scale, half);
+    } else {  // partials [2][nsplit][K/V heads][N][D]: dK (scaled) then dV
+      const size_t per = (size_t)nkvh * N * D;
+      const size_t off = (size_t)split * per + head_off + (size_t)my_k * D;
+      if (role == 0) store_rows_f32<D>(part + (size_t)nsplit * per + off, acc, 1.0f, half);
+      else store_rows_f32<D>(part + off, acc, scale, half);
+    }
   }
+}
+
+// ============================================================== split reduction
+// dK and dV as bf16 from the float32 partials of the workgroups that shared a
+// K/V head's query heads: out[e] = sum over splits j = 0, 1, ... in that order,
+// so the result is bitwise reproducible.  One thread per 8 elements.
+__global__ void __launch_bounds__(256)
+fa_bwd_reduce_kernel(const float *__restrict__ part, __bf16 *__restrict__ dK, __bf16 *__restrict__ dV,
+                     long long count, int nsplit) {
+  const long long chunks = count / 8;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * chunks) return;
+  const int which = i >= chunks;  // 0: dK, 1: dV
+  const long long e = (i - which * chunks) * 8;
+  const float *p = part + (size_t)which * nsplit * count + e;
+  floatx4 a = *reinterpret_cast<const floatx4 *>(p);
+  floatx4 b = *reinterpret_cast<const floatx4 *>(p + 4);
+  for (int j = 1; j < nsplit; ++j) {
+    a += *reinterpret_cast<const floatx4 *>(p + (size_t)j * count);
+    b += *reinterpret_cast<const floatx4 *>(p + (size_t)j * count + 4);
+  }
+  const u32x4 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+  *reinterpret_cast<u32x4 *>((which ? dV : dK) + e) = w;
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                  const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int H, int N, float scale,
-                  hipStream_t stream) {
-  const long long nbh = (long long)B * H;
+                  const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int H, int group, int N,
+                  float scale, hipStream_t stream) {
+  const long long nbh = (long long)B * H;          // query heads
+  const long long nkvh = nbh / group;              // K/V heads
+  const int nsplit = bwd_splits(nkvh, N, group);
   const long long gq = nbh * ((N + 127) / 128);
-  const long long gk = nbh * ((N + 127) / 128);
+  const long long gk = nkvh * nsplit * ((N + 127) / 128);
   if (gq > 0x7fffffffLL || gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = scale * kLog2e;
   float *dsum = ws;
   float *lse2 = ws + (size_t)nbh * N;
+  float *part = (nsplit > 1) ? ws + bwd_partial_offset_floats(nbh, N) : nullptr;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)gq), dim3(256), 0, stream,
                      (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)o,
-                     (const __bf16 *)dout, lse, (__bf16 *)dq, dsum, lse2, N, c, scale);
+                     (const __bf16 *)dout, lse, (__bf16 *)dq, dsum, lse2, N, group, c, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (D == 64)
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, stream,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
-                       (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, N, c, scale);
+                       (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
+                       nsplit, c, scale);
   else
     hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(512), 0, stream,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
-                       (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, N, c, scale);
+                       (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
+                       nsplit, c, scale);
+  if (nsplit == 1) return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long count = nkvh * (long long)N * D;
+  const long long threads = 2 * (count / 8);
+  hipLaunchKernelGGL(fa_bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     (const float *)part, (__bf16 *)dk, (__bf16 *)dv, count, nsplit);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                           const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int H, int N,
-                           int d, bool causal, float scale, hipStream_t stream) {
+                           const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int H, int group,
+                           int N, int d, bool causal, float scale, hipStream_t stream) {
   if (d == 64)
-    return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, stream)
-                  : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, stream);
-  return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, stream)
-                : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, stream);
+    return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream)
+                  : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream);
+  return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream)
+                : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream);
 }
 
 }  // namespace fa

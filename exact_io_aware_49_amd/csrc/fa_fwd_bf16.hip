@@ -73,7 +73,7 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE,
-                   int N, int nbh, float scale_log2e) {
+                   int N, int nbh, int group, float scale_log2e) {
   using C = FwdCfg<D>;
   constexpr int TB = C::TILE_BYTES;
   constexpr int RB = C::ROW_BYTES;
@@ -90,10 +90,11 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   int bh, qb;
   map_block(blockIdx.x, nqb, nbh, CAUSAL, bh, qb);
 
-  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const size_t head_off = (size_t)bh * (size_t)N * D;          // query head: Q, O
+  const size_t kv_off = (size_t)(bh / group) * (size_t)N * D;  // its K/V head (group query heads share one)
   const uint32_t head_bytes = (uint32_t)N * RB;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, head_bytes);
 
   const int q0 = qb * C::BR;       // first query row of the workgroup
   const int qw0 = q0 + wave * 32;  // first query row of this wave
@@ -347,15 +348,15 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
-                  float scale, hipStream_t stream) {
+hipError_t launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int group,
+                  int N, float scale, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int nbh = B * H;
   const int nqb = (N + C::BR - 1) / C::BR;
   const long long blocks = (long long)nqb * nbh;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, N, nbh,
+                     (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, N, nbh, group,
                      scale * kLog2e);
   return hipGetLastError();
 }
@@ -363,11 +364,11 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-                           int N, int d, bool causal, float scale, hipStream_t stream) {
-  if (d == 64) return causal ? launch<64, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                             : launch<64, false>(q, k, v, o, lse, B, H, N, scale, stream);
-  return causal ? launch<128, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                : launch<128, false>(q, k, v, o, lse, B, H, N, scale, stream);
+                           int group, int N, int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 64) return causal ? launch<64, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
+                             : launch<64, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
+  return causal ? launch<128, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
+                : launch<128, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
 }
 
 }  // namespace fa

@@ -35,7 +35,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256)
 fa_fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
-                  float *__restrict__ O, float *__restrict__ LSE, int N, float scale) {
+                  float *__restrict__ O, float *__restrict__ LSE, int N, int group, float scale) {
   constexpr int KS = D + 4;  // padded K row (floats)
   constexpr int CPL = D / 64;  // output columns per lane
   __shared__ __align__(16) float Qs[F_BR * D];
@@ -49,7 +49,8 @@ fa_fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K, cons
   const int nqb = (N + F_BR - 1) / F_BR;
   const int bh = blockIdx.x / nqb;
   const int qb = blockIdx.x % nqb;
-  const size_t head_off = (size_t)bh * N * D;
+  const size_t head_off = (size_t)bh * N * D;           // query head: Q, O
+  const size_t kv_off = (size_t)(bh / group) * N * D;   // its K/V head (group query heads share one)
   const int q0 = qb * F_BR;
   const int qw0 = q0 + wave * F_ROWS;
 
@@ -80,8 +81,8 @@ fa_fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K, cons
       const int r = e / (D / 4), c4 = e % (D / 4);
       floatx4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
       if (kb + r < N) {
-        kv = *reinterpret_cast<const floatx4 *>(K + head_off + (size_t)(kb + r) * D + 4 * c4);
-        vv = *reinterpret_cast<const floatx4 *>(V + head_off + (size_t)(kb + r) * D + 4 * c4);
+        kv = *reinterpret_cast<const floatx4 *>(K + kv_off + (size_t)(kb + r) * D + 4 * c4);
+        vv = *reinterpret_cast<const floatx4 *>(V + kv_off + (size_t)(kb + r) * D + 4 * c4);
       }
       *reinterpret_cast<floatx4 *>(Ks + r * KS + 4 * c4) = kv;
       *reinterpret_cast<floatx4 *>(Vs + r * D + 4 * c4) = vv;
@@ -158,23 +159,23 @@ fa_fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K, cons
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
-                  float scale, hipStream_t stream) {
+hipError_t launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int group,
+                  int N, float scale, hipStream_t stream) {
   const long long blocks = (long long)((N + F_BR - 1) / F_BR) * B * H;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const float *)q, (const float *)k, (const float *)v, (float *)o, lse, N, scale);
+                     (const float *)q, (const float *)k, (const float *)v, (float *)o, lse, N, group, scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-                          int N, int d, bool causal, float scale, hipStream_t stream) {
-  if (d == 64) return causal ? launch<64, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                             : launch<64, false>(q, k, v, o, lse, B, H, N, scale, stream);
-  return causal ? launch<128, true>(q, k, v, o, lse, B, H, N, scale, stream)
-                : launch<128, false>(q, k, v, o, lse, B, H, N, scale, stream);
+                          int group, int N, int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 64) return causal ? launch<64, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
+                             : launch<64, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
+  return causal ? launch<128, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
+                : launch<128, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
 }
 
 }  // namespace fa

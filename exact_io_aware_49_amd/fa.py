@@ -1,7 +1,8 @@
 """Thin ctypes binding of libfa.so (include/fa.h).
 
-The functions `fa_fwd`, `fa_bwd`, `fa_bwd_workspace_size`, `fa_status_string`
-and `fa_version` mirror the C ABI one to one: they take raw device pointers
+The functions `fa_fwd`, `fa_bwd`, `fa_bwd_workspace_size`, their shared-K/V-head
+forms `fa_fwd_gqa`, `fa_bwd_gqa`, `fa_bwd_gqa_workspace_size`, and
+`fa_status_string` and `fa_version` mirror the C ABI one to one: they take raw device pointers
 (ints), sizes and a stream handle, and return the status code.  `forward` and
 `backward` are the torch-facing conveniences: they check devices, dtypes and
 shapes, allocate outputs (and the backward workspace) with torch on the
@@ -54,6 +55,12 @@ def load_library(path: str = LIB_PATH):
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_gqa.restype = i
+    lib.fa_bwd_gqa_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa_bwd_gqa_workspace_size.restype = sz
+    lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_gqa.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -76,6 +83,20 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, 
            stream) -> int:
     return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                                  causal, scale, dtype, stream)
+
+
+def fa_fwd_gqa(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream) -> int:
+    return load_library().fa_fwd_gqa(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream)
+
+
+def fa_bwd_gqa_workspace_size(B, Hq, Hkv, N, d, dtype) -> int:
+    return load_library().fa_bwd_gqa_workspace_size(B, Hq, Hkv, N, d, dtype)
+
+
+def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d, causal, scale,
+               dtype, stream) -> int:
+    return load_library().fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                                     N, d, causal, scale, dtype, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -122,15 +143,26 @@ def default_scale(d: int) -> float:
     return float(d) ** -0.5
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """Exact attention forward on the GPU.  q, k, v: [B, H, N, d] (bf16 or fp32).
+def _kv_heads(q, k, v):
+    """Number of K/V heads: k and v are [B, Hkv, N, d] with Hkv dividing q's head count."""
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise RuntimeError("q [B, Hq, N, d] and k, v [B, Hkv, N, d] must share dtype")
+    B, H, N, d = q.shape
+    hkv = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d) or hkv < 1 or H % hkv != 0:
+        raise RuntimeError("k, v must be [B, Hkv, N, d] with Hkv dividing the query head count")
+    return hkv
 
-    Returns (o, lse): o like q, lse float32 [B, H, N].
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Exact attention forward on the GPU.  q: [B, Hq, N, d], k, v: [B, Hkv, N, d] (bf16 or fp32),
+    Hkv dividing Hq (query head h uses K/V head h // (Hq / Hkv); Hkv = Hq is plain multi-head).
+
+    Returns (o, lse): o like q, lse float32 [B, Hq, N].
     """
     load_library()
     _check_tensors(q, k, v)
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise RuntimeError("q, k, v must share shape [B, H, N, d] and dtype")
+    hkv = _kv_heads(q, k, v)
     B, H, N, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
@@ -138,28 +170,29 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     _check_tensors(q, o, lse_t)
     if o.shape != q.shape or o.dtype != q.dtype or lse_t.shape != (B, H, N) or lse_t.dtype != torch.float32:
         raise RuntimeError("out / lse have the wrong shape or dtype")
-    _check(fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(), B, H, N, d,
-                  int(bool(causal)), scale, _dtype_code(q), _stream_handle(q.device)))
+    _check(fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(), B, H, hkv, N,
+                      d, int(bool(causal)), scale, _dtype_code(q), _stream_handle(q.device)))
     return o, lse_t
 
 
 def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, workspace=None):
-    """Exact attention backward with recomputation.  Returns (dq, dk, dv) like q."""
+    """Exact attention backward with recomputation.  Returns (dq like q, dk and dv like k)."""
     load_library()
     _check_tensors(q, k, v, o, do, lse)
-    for t in (k, v, o, do):
+    hkv = _kv_heads(q, k, v)
+    for t in (o, do):
         if t.shape != q.shape or t.dtype != q.dtype:
-            raise RuntimeError("q, k, v, o, do must share shape [B, H, N, d] and dtype")
+            raise RuntimeError("o and do must match q [B, Hq, N, d]")
     B, H, N, d = q.shape
     if lse.shape != (B, H, N) or lse.dtype != torch.float32:
         raise RuntimeError("lse must be float32 [B, H, N]")
     scale = default_scale(d) if scale is None else float(scale)
     code = _dtype_code(q)
-    need = fa_bwd_workspace_size(B, H, N, d, code)
+    need = fa_bwd_gqa_workspace_size(B, H, hkv, N, d, code)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                  B, H, N, d, int(bool(causal)), scale, code, _stream_handle(q.device)))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                      B, H, hkv, N, d, int(bool(causal)), scale, code, _stream_handle(q.device)))
     return dq, dk, dv

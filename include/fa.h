@@ -57,7 +57,7 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL_POINTER = 1,         /* a required pointer is NULL */
-  FA_ERR_BAD_SHAPE = 2,            /* B, H or N < 1, or the element count overflows */
+  FA_ERR_BAD_SHAPE = 2,            /* B, H or N < 1, the element count overflows, or Hq % Hkv != 0 */
   FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128} */
   FA_ERR_UNSUPPORTED_DTYPE = 4,    /* dtype unknown, or not supported by this entry point */
   FA_ERR_BAD_SCALE = 5,            /* scale not finite or not > 0 */
@@ -114,6 +114,39 @@ FA_API int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            void *workspace, size_t workspace_bytes,
            int B, int H, int N, int d, int causal, float scale, int dtype,
            void *stream);
+
+/*
+ * Query heads sharing key/value heads (multi-query attention, which
+ * "FlashAttention (DE)", section "Evolution und Weiterentwicklungen", lists
+ * among the FlashAttention-2 capabilities, and its grouped generalisation).
+ * There are Hq query heads and Hkv key/value heads, Hkv >= 1 dividing Hq;
+ * query head h attends with K/V head h / (Hq / Hkv) (contiguous groups).
+ * Hkv = 1 is multi-query attention; Hkv = Hq is exactly fa_fwd / fa_bwd, which
+ * are these calls with Hq = Hkv = H.
+ *
+ *   q, o, dout, dq : [B,Hq,N,d];  k, v, dk, dv : [B,Hkv,N,d];  lse : [B,Hq,N].
+ *
+ * The gradient of a shared K/V head is the sum over its query heads; the
+ * kernel that owns a block of keys runs over the query heads of the group.
+ * When B*Hkv*ceil(N/128) key blocks are too few to fill the GPU, the group's
+ * query heads are split over S = min(Hq/Hkv, ceil(512 / (B*Hkv*ceil(N/128))))
+ * workgroups per key block, each writing float32 partial dk and dv into the
+ * workspace, and a third kernel sums the S partials in a fixed order.  No
+ * atomics are used, so dq, dk and dv are bitwise reproducible.
+ * fa_bwd_gqa_workspace_size = 2*B*Hq*N*4 bytes rounded up to 256, plus
+ * 2*S*B*Hkv*N*d*4 bytes when S > 1.  Hkv < 1 or Hq not a multiple of Hkv gives
+ * FA_ERR_BAD_SHAPE.  Everything else is as for fa_fwd / fa_bwd_workspace_size
+ * / fa_bwd.
+ */
+FA_API int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               int dtype, void *stream);
+FA_API size_t fa_bwd_gqa_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype);
+FA_API int fa_bwd_gqa(const void *q, const void *k, const void *v, const void *o,
+               const void *dout, const float *lse, void *dq, void *dk, void *dv,
+               void *workspace, size_t workspace_bytes,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               int dtype, void *stream);
 
 /* A static, human-readable string for a status code (never NULL). */
 FA_API const char *fa_status_string(int status);

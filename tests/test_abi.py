@@ -27,7 +27,8 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     lib = fa.load_library()
     names = declared_symbols()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_version"}
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_gqa", "fa_bwd_gqa",
+                          "fa_bwd_gqa_workspace_size", "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(lib, n), n
     raw = ctypes.CDLL(fa.LIB_PATH)
@@ -78,6 +79,56 @@ def test_fwd_validation(kw, code):
 ])
 def test_bwd_validation(kw, code):
     assert bwd(**kw) == code
+
+
+def fwd_gqa(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=8, Hkv=2, N=128, d=64, causal=0, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"],
+                         a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+def bwd_gqa(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, wsb=1 << 20, B=1, Hq=8, Hkv=2, N=128,
+             d=64, causal=1, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_gqa(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                         a["wsb"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"],
+                         a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), 1), (dict(Hkv=0), 2), (dict(Hkv=-2), 2), (dict(Hkv=3), 2), (dict(Hkv=16), 2),
+    (dict(Hq=0), 2), (dict(d=80), 3), (dict(dtype=3), 4), (dict(scale=0.0), 5), (dict(v=P + 4), 6),
+    (dict(causal=2), 8),
+])
+def test_fwd_gqa_validation(kw, code):
+    assert fwd_gqa(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=None), 1), (dict(Hkv=3), 2), (dict(Hkv=0), 2), (dict(dtype=0), 4), (dict(wsb=100), 7),
+    (dict(dv=P + 8), 6),
+])
+def test_bwd_gqa_validation(kw, code):
+    assert bwd_gqa(**kw) == code
+
+
+def test_gqa_workspace_size():
+    # documented in include/fa.h: 2*B*Hq*N*4 bytes (rounded to 256), plus
+    # 2*S*B*Hkv*N*d*4 bytes of split partials when S = min(Hq/Hkv,
+    # ceil(512 / (B*Hkv*ceil(N/128)))) exceeds 1
+    def expect(B, hq, hkv, N, d):
+        base = (2 * B * hq * N * 4 + 255) // 256 * 256
+        blocks = B * hkv * ((N + 127) // 128)
+        s = min(hq // hkv, max(1, (512 + blocks - 1) // blocks))
+        return base + (2 * s * B * hkv * N * d * 4 if s > 1 else 0)
+    for args in [(2, 32, 4, 2048, 128), (2, 16, 1, 1024, 64), (8, 64, 8, 4096, 128), (1, 3, 1, 77, 64)]:
+        assert fa.fa_bwd_gqa_workspace_size(*args, 1) == expect(*args), args
+    assert fa.fa_bwd_gqa_workspace_size(2, 32, 4, 2048, 128, 1) == 2 * 2 * 32 * 2048 * 4 + 2 * 4 * 8 * 2048 * 128 * 4
+    assert fa.fa_bwd_gqa_workspace_size(8, 64, 8, 4096, 128, 1) == 2 * 8 * 64 * 4096 * 4   # enough key blocks: no split
+    assert fa.fa_bwd_gqa_workspace_size(2, 32, 5, 2048, 128, 1) == 0
+    assert fa.fa_bwd_gqa_workspace_size(2, 32, 32, 2048, 128, 1) == fa.fa_bwd_workspace_size(2, 32, 2048, 128, 1)
 
 
 def test_workspace_size():

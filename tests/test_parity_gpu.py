@@ -133,6 +133,84 @@ def test_bwd_encoder_shape():
     check_bwd_heads(q, k, v, do, False, w.scale, [(0, 0), (3, 15)], "bwd_encoder_b4h16n4096d128")
 
 
+# ------------------------------------------------------------------ shared K/V heads
+
+def _gqa_check(case_name, heads_b0):
+    """Forward and backward of one shared-K/V-head case, checked on batch 0 for the
+    K/V heads in `heads_b0` (every query head of each such group).
+
+    dK and dV of a shared head are sums over its query heads, so they grow with
+    the group (|dK| reaches ~10 at 8 query heads per K/V head, against ~1 for one
+    head), and storing a value of magnitude M in bf16 alone costs up to M * 2^-9.
+    Their absolute bound is therefore scaled by max(1, max|ref|); the relative L2
+    bound (1e-2) is unchanged.  O, lse and dQ keep the plain bounds."""
+    c = inputs.GQA_CASES[case_name]
+    B, hq, hkv, N, d, causal = c["B"], c["hq"], c["hkv"], c["N"], c["d"], c["causal"]
+    g = hq // hkv
+    q, k, v, do = inputs.gen_gqa(B, hq, hkv, N, d, "bf16", c["seed"], with_do=True)
+    say(f"[gqa] {case_name} B={B} Hq={hq} Hkv={hkv} N={N} d={d} causal={causal} K/V heads checked={heads_b0}")
+    qd, kd, vd, dod = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16")
+    scale = d ** -0.5
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (host(t) for t in (o, lse, dq, dk, dv))
+    assert dk.shape == (B, hkv, N, d) and dq.shape == (B, hq, N, d)
+    s = f32(scale)
+    for hk in heads_b0:
+        qs = slice(hk * g, (hk + 1) * g)
+        sq = (slice(0, 1), qs)
+        sk = (slice(0, 1), slice(hk, hk + 1))
+        ro, rl = oracle.attention_forward(q[sq], k[sk], v[sk], causal, s)
+        rq, rk, rv = oracle.attention_backward(q[sq], k[sk], v[sk], do[sq], causal, s)
+        worst = {}
+        for name, got, ref, is_lse in (("O", o[sq], ro, False), ("lse", lse[sq], rl, True), ("dQ", dq[sq], rq, False),
+                                       ("dK", dk[sk], rk, False), ("dV", dv[sk], rv, False)):
+            worst[name] = assert_close(f"{case_name} {name} kv head {hk}", got, ref, "bf16", lse=is_lse,
+                                       magnitude_scaled=name in ("dK", "dV"))
+            worst[name] = worst[name] + (float(np.abs(ref).max()),)
+        say("   kv head %d: " % hk + "  ".join(f"{n} max/rel {e[0]:.2e}/{e[1]:.2e} (max|ref| {e[2]:.2f})"
+                                               for n, e in worst.items()))
+    # every K/V head: the gradient identities of the exact result
+    assert np.abs(dk.sum(axis=2)).max() < 0.5
+    dosum = do.astype(np.float64).reshape(B, hkv, g, N, d).sum(axis=(2, 3))
+    assert np.abs(dv.sum(axis=2) - dosum).max() < 0.5
+
+
+def test_gqa_causal_d128():
+    """8 query heads per K/V head, causal, d = 128 (the paired-wave dK/dV kernel)."""
+    need_gpu()
+    _gqa_check("gqa_causal_b2hq32hkv4n2048d128", [0, 3])
+
+
+def test_mqa_d64():
+    """Multi-query attention: 16 query heads over one K/V head, d = 64."""
+    need_gpu()
+    _gqa_check("mqa_b2hq16hkv1n1024d64", [0])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_sweep(d, causal):
+    """Ragged lengths and group sizes 1..4 against the oracle on every head (dK and dV
+    with the magnitude-scaled absolute bound, as in the cases above)."""
+    need_gpu()
+    for i, (N, hq, hkv) in enumerate([(1, 2, 1), (17, 4, 2), (100, 3, 1), (129, 4, 1), (200, 2, 2)]):
+        q, k, v, do = inputs.gen_gqa(1 + i % 2, hq, hkv, N, d, "bf16", 1200 + 5 * i + d, with_do=True)
+        qd, kd, vd, dod = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16")
+        o, lse = fa.forward(qd, kd, vd, causal=causal)
+        dq, dk, dv = fa.backward(qd, kd, vd, o, dod, lse, causal=causal)
+        torch.cuda.synchronize()
+        s = f32(d ** -0.5)
+        ro, rl = oracle.attention_forward(q, k, v, causal, s)
+        rq, rk, rv = oracle.attention_backward(q, k, v, do, causal, s)
+        tag = f"gqa sweep N={N} Hq={hq} Hkv={hkv}"
+        say(f"[gqa] {tag} d={d} causal={causal}")
+        for name, got, ref, is_lse in (("O", o, ro, False), ("lse", lse, rl, True), ("dQ", dq, rq, False),
+                                       ("dK", dk, rk, False), ("dV", dv, rv, False)):
+            assert_close(f"{tag} {name}", host(got), ref, "bf16", lse=is_lse, magnitude_scaled=name in ("dK", "dV"))
+
+
 # ------------------------------------------------------------------ small sweeps
 
 SWEEP_N = [1, 17, 64, 100, 128, 129, 255, 300]
