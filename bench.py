@@ -2,6 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
+--workload also accepts the shared-K/V-head cases (query heads grouped over
+fewer K/V heads), e.g. gqa_causal_b2hq32hkv4n2048d128; they are timed the same
+way through fa_fwd_gqa / fa_bwd_gqa.
+
 A step runs the whole path once over one batch of synthetic inputs that are
 already resident in device memory: fa_fwd (O, lse) then fa_bwd (dQ, dK, dV,
 recomputing the score blocks from lse).  Workload: the non-causal
@@ -70,9 +74,8 @@ def fwd_flops(B, H, N, d, causal):
 
 
 def cpu_baseline(w, budget_s: float):
-    """Time the float64 oracle (forward + backward) on whole heads until ~budget_s elapse."""
+    """Time the float64 oracle (forward + backward) on whole query heads until ~budget_s elapse."""
     import oracle
-    from exact_io_aware_49_amd import inputs
 
     try:
         from threadpoolctl import threadpool_info
@@ -80,15 +83,17 @@ def cpu_baseline(w, budget_s: float):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     B, H, N, d = w.shape
-    q, k, v, do = inputs.gen_qkv(w.shape, w.dtype, w.seed, with_do=True)
+    q, k, v, do = w.inputs()
+    g = H // k.shape[1]
     s = float(np.float32(w.scale))
     heads = 0
     t0 = time.perf_counter()
     for b in range(B):
         for h in range(H):
-            sl = (slice(b, b + 1), slice(h, h + 1))
-            oracle.attention_forward(q[sl], k[sl], v[sl], w.causal, s)
-            oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], w.causal, s)
+            sq = (slice(b, b + 1), slice(h, h + 1))
+            sk = (slice(b, b + 1), slice(h // g, h // g + 1))
+            oracle.attention_forward(q[sq], k[sk], v[sk], w.causal, s)
+            oracle.attention_backward(q[sq], k[sk], v[sk], do[sq], w.causal, s)
             heads += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -101,9 +106,32 @@ def cpu_baseline(w, budget_s: float):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{heads} of {B * H} heads (B={B},H={H},N={N},d={d}), float64 numpy forward+backward, "
+        "sample": f"{heads} of {B * H} query heads (B={B},H={H},N={N},d={d}), float64 numpy forward+backward, "
                   f"{dt:.1f} s wall",
     }
+
+
+class _Case:
+    """One benchmark workload: a named workload, or a shared-K/V-head case."""
+
+    def __init__(self, name):
+        from exact_io_aware_49_amd import inputs
+        self.name = name
+        if name in inputs.WORKLOADS:
+            w = inputs.WORKLOADS[name]
+            self.B, self.H, self.N, self.d = w.shape
+            self.hkv, self.causal, self.scale, self.seed = w.H, w.causal, w.scale, w.seed
+        elif name in inputs.GQA_CASES:
+            c = inputs.GQA_CASES[name]
+            self.B, self.H, self.N, self.d = c["B"], c["hq"], c["N"], c["d"]
+            self.hkv, self.causal, self.scale, self.seed = c["hkv"], c["causal"], c["d"] ** -0.5, c["seed"]
+        else:
+            raise SystemExit(f"unknown workload {name}")
+        self.shape = (self.B, self.H, self.N, self.d)
+
+    def inputs(self):
+        from exact_io_aware_49_amd import inputs
+        return inputs.gen_gqa(self.B, self.H, self.hkv, self.N, self.d, "bf16", self.seed, with_do=True)
 
 
 def main(argv=None):
@@ -126,39 +154,38 @@ def main(argv=None):
     import torch
 
     import exact_io_aware_49_amd as fa
-    from exact_io_aware_49_amd import inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     fa.load_library()
-    w = inputs.WORKLOADS[a.workload]
+    w = _Case(a.workload)
     B, H, N, d = w.shape
+    hkv = w.hkv
     causal = int(w.causal)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    q, k, v, do = (torch.from_numpy(x).to(dev).to(torch.bfloat16)
-                   for x in inputs.gen_qkv(w.shape, "bf16", w.seed, with_do=True))
+    q, k, v, do = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in w.inputs())
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws_bytes = fa.fa_bwd_workspace_size(B, H, N, d, fa.FA_DTYPE_BF16)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_bwd_gqa_workspace_size(B, H, hkv, N, d, fa.FA_DTYPE_BF16)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     scale = float(w.scale)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
     def fwd():
-        rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
-                       causal, scale, fa.FA_DTYPE_BF16, sh)
+        rc = fa.fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, hkv, N,
+                           d, causal, scale, fa.FA_DTYPE_BF16, sh)
         if rc:
             raise RuntimeError(fa.fa_status_string(rc))
 
     def bwd():
-        rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N, d,
-                       causal, scale, fa.FA_DTYPE_BF16, sh)
+        rc = fa.fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws_bytes, B, H, hkv, N, d,
+                           causal, scale, fa.FA_DTYPE_BF16, sh)
         if rc:
             raise RuntimeError(fa.fa_status_string(rc))
 
@@ -214,7 +241,7 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic: i.i.d. N(0,1) from PCG64, rounded to bf16, resident in HBM",
         "config": {"workload": w.name, "pass": "forward+backward", "B": B, "H": H, "N": N, "d": d,
-                   "causal": bool(w.causal), "scale": scale},
+                   "causal": bool(w.causal), "scale": scale, **({"Hkv": hkv} if hkv != H else {})},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(fwd_tf, 2),
