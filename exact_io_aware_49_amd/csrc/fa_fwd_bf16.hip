@@ -9,6 +9,11 @@
 // exponential sum per row, and writes only O and lse.  The N x N scores never
 // leave registers.
 //
+// Head dims 64, 128 and 256.  At d = 256 a wave's Q fragments (64 registers),
+// output accumulator (128) and two score tiles (64) leave no room for a second
+// wave per SIMD or for a second LDS fragment set, so that instantiation runs
+// one wave per SIMD and reads each chunk's fragments just before use.
+//
 // Mapping to one workgroup (4 waves, 256 threads), BR = 128 query rows:
 //   * Each wave owns 32 query rows.  Its Q rows sit in VGPRs as the B operand
 //     of S^T = K Q^T (lane = query row, 8 consecutive head-dim slots per lane).
@@ -62,15 +67,15 @@ struct FwdCfg {
 // Chunk permutations (physical chunk = logical chunk ^ swz(row)).
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-  return (D == 128) ? (r & 15) : ((r >> 1) & 7);
+  return (D >= 128) ? (r & 15) : ((r >> 1) & 7);
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
-  return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return (D >= 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, (D == 256) ? 1 : 2)
 fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE,
                    int N, int nbh, int group, float scale_log2e) {
@@ -210,13 +215,14 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     }
   };
   auto frag_wait = [&](Frag &f) {
-    static_assert(QK_PER_CH == 4 || QK_PER_CH == 2, "fragment sizes");
-    static_assert(C::CT == 4 || C::CT == 2, "fragment sizes");
-    if constexpr (QK_PER_CH == 4 && C::CT == 4)
-      lds_wait_all(f.k[0], f.k[1], f.k[2], f.k[3], f.v[0][0], f.v[0][1], f.v[1][0], f.v[1][1], f.v[2][0],
-                   f.v[2][1], f.v[3][0], f.v[3][1]);
-    else
-      lds_wait_all(f.k[0], f.k[1], f.v[0][0], f.v[0][1], f.v[1][0], f.v[1][1]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < QK_PER_CH; ++i) redefine(f.k[i]);
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+      redefine(f.v[ct][0]);
+      redefine(f.v[ct][1]);
+    }
   };
 
   // One tile step.  BUF is the V buffer of tile t (and the K buffer of tile t).
@@ -231,7 +237,8 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const bool act = !CAUSAL || (kb <= qw0 + 31);
 
     Frag fa, fb;
-    if (act) read_frag(bufc, std::integral_constant<int, 0>{}, fa);
+    constexpr bool AHEAD = D < 256;  // at d = 256 a second fragment set does not fit
+    if (AHEAD && act) read_frag(bufc, std::integral_constant<int, 0>{}, fa);
     float mc = 0.f;
     if (act) {
       // ---- masking (diagonal and ragged tiles only)
@@ -293,8 +300,9 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         Frag &f = (CH % 2 == 0) ? fa : fb;
         Frag &g = (CH % 2 == 0) ? fb : fa;
         const bf16x8 pb = chunk_p(CH / 2, CH % 2);
+        if constexpr (!AHEAD) read_frag(bufc, cc, f);
         frag_wait(f);
-        if constexpr (CH + 1 < NCH) read_frag(bufc, std::integral_constant<int, CH + 1>{}, g);
+        if constexpr (AHEAD && CH + 1 < NCH) read_frag(bufc, std::integral_constant<int, CH + 1>{}, g);
         constexpr int first = CH * QK_PER_CH;
         constexpr int kt = first / C::KSTEPS;
         constexpr int k0 = first % C::KSTEPS;
@@ -367,6 +375,8 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
                            int group, int N, int d, bool causal, float scale, hipStream_t stream) {
   if (d == 64) return causal ? launch<64, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
                              : launch<64, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
+  if (d == 256) return causal ? launch<256, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
+                              : launch<256, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
   return causal ? launch<128, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
                 : launch<128, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
 }

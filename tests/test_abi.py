@@ -62,7 +62,7 @@ def bwd(**kw):
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
     (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(B=1 << 30, H=1 << 30), 2),
     (dict(N=1 << 24, d=64), 2), (dict(N=1 << 23, d=128, dtype=1), 2), (dict(N=(1 << 22) + 64, d=128, dtype=0), 2),
-    (dict(d=32), 3), (dict(d=96), 3), (dict(d=256), 3),
+    (dict(d=32), 3), (dict(d=96), 3), (dict(d=512), 3), (dict(d=256, dtype=0), 3),
     (dict(dtype=2), 4), (dict(dtype=-1), 4),
     (dict(scale=0.0), 5), (dict(scale=-0.125), 5), (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5),
     (dict(q=P + 8), 6), (dict(o=P + 2), 6), (dict(lse=P + 4), 6),
@@ -74,7 +74,7 @@ def test_fwd_validation(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(do=None), 1), (dict(dq=None), 1), (dict(lse=None), 1),
-    (dict(N=0), 2), (dict(d=80), 3), (dict(dtype=0), 4), (dict(scale=0.0), 5),
+    (dict(N=0), 2), (dict(d=80), 3), (dict(d=256), 3), (dict(dtype=0), 4), (dict(scale=0.0), 5),
     (dict(ws=None), 7), (dict(wsb=100), 7), (dict(dk=P + 8), 6), (dict(ws=P + 8), 6), (dict(causal=3), 8),
 ])
 def test_bwd_validation(kw, code):
@@ -136,6 +136,7 @@ def test_workspace_size():
     assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 1) == 256
     assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 0) == 0   # fp32 backward unsupported
     assert fa.fa_bwd_workspace_size(1, 1, 3, 96, 1) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 256, 1) == 0  # head dim 256: forward only
     assert fa.fa_bwd_workspace_size(0, 1, 3, 64, 1) == 0
 
 

@@ -133,6 +133,33 @@ def test_bwd_encoder_shape():
     check_bwd_heads(q, k, v, do, False, w.scale, [(0, 0), (3, 15)], "bwd_encoder_b4h16n4096d128")
 
 
+# ------------------------------------------------------------------ head dim 256 (forward)
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_d256_sweep(causal):
+    """Head dim 256, bf16 forward: ragged lengths against the oracle on every output."""
+    need_gpu()
+    for i, N in enumerate([1, 17, 64, 100, 129, 300]):
+        q, k, v = inputs.gen_qkv((1 + i % 2, 1 + i % 3, N, 256), "bf16", 1300 + 7 * i)
+        check_fwd_full(q, k, v, causal, 256 ** -0.5, "bf16", f"d256 sweep N={N}")
+
+
+def test_fwd_d256_heads():
+    """Head dim 256 at B=2 H=8 N=2048, causal, with query heads sharing K/V heads (4 per K/V
+    head): whole heads of batch 0 against the oracle."""
+    need_gpu()
+    B, hq, hkv, N, d = 2, 8, 2, 2048, 256
+    q, k, v = inputs.gen_gqa(B, hq, hkv, N, d, "bf16", 41)
+    say(f"[fwd] d256 B={B} Hq={hq} Hkv={hkv} N={N} causal")
+    o, lse = fa.forward(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), causal=True)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    ro, rl = oracle.attention_forward(q[:1], k[:1], v[:1], True, f32(d ** -0.5))
+    eo = assert_close("d256 O", o[:1], ro, "bf16")
+    el = assert_close("d256 lse", lse[:1], rl, "bf16", lse=True)
+    say(f"   O max/rel {eo[0]:.2e}/{eo[1]:.2e}  lse max {el[0]:.2e}")
+
+
 # ------------------------------------------------------------------ shared K/V heads
 
 def _gqa_check(case_name, heads_b0):
