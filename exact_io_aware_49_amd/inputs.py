@@ -125,6 +125,33 @@ GQA_CASES = {
 }
 
 
+def gen_decode(B: int, hq: int, hkv: int, nq: int, nk: int, d: int, seed: int, min_len: int | None = None):
+    """Inputs of attention against a key/value cache, bf16-valued: Q [B,hq,nq,d], K and V
+    [B,hkv,nk,d] (cache capacity nk), drawn in that order, then per-batch cache lengths
+    (int32 [B]) uniform in [min_len, nk] (all nk when min_len is None)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for shp in [(B, hq, nq, d), (B, hkv, nk, d), (B, hkv, nk, d)]:
+        out.append(bf16_round(rng.standard_normal(size=shp, dtype=np.float32)))
+    if min_len is None:
+        lens = np.full(B, nk, dtype=np.int32)
+    else:
+        lens = rng.integers(min_len, nk + 1, size=B).astype(np.int32)
+    return out + [lens]
+
+
+# Decode shapes (new query rows against a key/value cache) used by the parity
+# tests and the benchmark: one new token per sequence with 8 query heads per
+# K/V head and ragged cache lengths (a 32-head, 8-K/V-head decoder at 8K
+# context), and four speculative tokens per sequence, causal, over a 4K cache.
+DECODE_CASES = {
+    "decode_b16hq32hkv8nk8192d128": dict(B=16, hq=32, hkv=8, nq=1, nk=8192, d=128, causal=False, min_len=4096,
+                                         seed=51),
+    "decode_spec4_causal_b8hq16hkv16nk4096d64": dict(B=8, hq=16, hkv=16, nq=4, nk=4096, d=64, causal=True,
+                                                     min_len=None, seed=52),
+}
+
+
 def workload_inputs(w: Workload):
     """Inputs of a named workload: Q, K, V (and dO for a backward workload)."""
     return gen_qkv(w.shape, w.dtype, w.seed, with_do=(w.kind == "bwd"))

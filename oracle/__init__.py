@@ -31,4 +31,6 @@ from .attention import (  # noqa: F401
     attention_backward_from_probs,
     kv_head,
     group_sum,
+    decode_positions,
+    attention_decode,
 )

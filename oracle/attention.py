@@ -241,3 +241,49 @@ def attention_backward(q, k, v, do, causal: bool, scale: float):
             dq[b, h], dk[b, h], dv[b, h] = attention_backward_from_probs(
                 p, q[b, h], k[b, hk], v[b, hk], do[b, h], scale)
     return dq, group_sum(dk, hkv), group_sum(dv, hkv)
+
+
+def decode_positions(length: int, nq: int) -> np.ndarray:
+    """Positions of nq new query rows appended to a cache of `length` rows: length - nq + i.
+
+    Reading of attention over a key/value cache in streaming generation
+    ("FlashAttention (DE)", section "Evolution und Weiterentwicklungen",
+    subsection "Spezialisierte Lösungen", FlashInfer): the new queries are the
+    last nq positions of the sequence whose keys and values the cache holds.
+    """
+    return int(length) - int(nq) + np.arange(int(nq))
+
+
+def attention_decode(q, k, v, kv_lens, causal: bool, scale: float):
+    """Attention of Nq query rows against a key/value cache.
+
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d] with Nk the cache capacity;
+    kv_lens: per-batch count L_b of valid cache rows (None = Nk for every
+    batch).  Query i of batch b sits at position L_b - Nq + i; it sees cache
+    rows j < L_b, and with `causal` only j <= L_b - Nq + i.  Query heads share
+    K/V heads as in attention_forward.  A query that sees no row gets O = 0 and
+    lse = -inf.  Returns (O [B,Hq,Nq,d], lse [B,Hq,Nq]) float64.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H, nq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    lens = [nk] * B if kv_lens is None else [int(x) for x in np.asarray(kv_lens).reshape(-1)]
+    if len(lens) != B or any(x < 0 or x > nk for x in lens):
+        raise ValueError("kv_lens must hold B values in [0, Nk]")
+    o = np.zeros((B, H, nq, v.shape[3]), dtype=np.float64)
+    lse = np.full((B, H, nq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        length = lens[b]
+        if length == 0:
+            continue
+        for h in range(H):
+            hk = kv_head(h, H, hkv)
+            s = scores(q[b, h], k[b, hk, :length], scale)
+            if causal:
+                s = causal_mask(s, decode_positions(length, nq))
+            p, m, l = softmax_rows(s)
+            o[b, h] = p @ np.asarray(v[b, hk, :length], dtype=np.float64)
+            lse[b, h] = _lse(m, l)
+    return o, lse

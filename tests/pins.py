@@ -327,6 +327,63 @@ def pin_gqa_finite_differences():
     return out
 
 
+# --------------------------------------------------------------------------- key/value cache (decode)
+
+def brute_decode(q, k, v, length, causal, scale):
+    """Pure-Python attention of the rows of q against the first `length` rows of k, v, the
+    queries being the last len(q) positions (query i at length - len(q) + i)."""
+    nq, dv = len(q), len(v[0])
+    o, lse = [], []
+    for i in range(nq):
+        pos = length - nq + i
+        vis = [j for j in range(length) if (not causal or j <= pos)]
+        if not vis:
+            o.append([0.0] * dv)
+            lse.append(-math.inf)
+            continue
+        sc = [scale * math.fsum(q[i][c] * k[j][c] for c in range(len(q[i]))) for j in vis]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        tot = math.fsum(w)
+        o.append([math.fsum(w[t] * v[j][c] for t, j in enumerate(vis)) / tot for c in range(dv)])
+        lse.append(mx + math.log(tot))
+    return o, lse
+
+
+def pin_decode_brute_force():
+    """Per-batch cache lengths, last-positions alignment, shared K/V heads: against the
+    pure-Python loop, head by head."""
+    out = []
+    r = _rng(23)
+    for (hq, hkv), nq, causal in itertools.product(((2, 1), (2, 2)), (1, 3), (False, True)):
+        B, nk, d = 3, 9, 3
+        lens = [9, 4, 2]  # 2 < nq = 3: the first query of that batch sees nothing when causal
+        q = r.standard_normal((B, hq, nq, d))
+        k, v = (r.standard_normal((B, hkv, nk, d)) for _ in range(2))
+        o, lse = A.attention_decode(q, k, v, np.array(lens), causal, 0.6)
+        for b in range(B):
+            for h in range(hq):
+                g = (h * hkv) // hq
+                bo, bl = brute_decode(q[b, h].tolist(), k[b, g].tolist(), v[b, g].tolist(), lens[b], causal, 0.6)
+                err = max(_maxdiff(o[b, h], bo), _maxdiff(lse[b, h], bl))
+                _fail_if(not err <= 1e-14, f"decode brute force Hq={hq} Hkv={hkv} nq={nq} causal={causal} "
+                                           f"b={b} h={h}: {err:.3e}", out)
+    return out
+
+
+def pin_decode_reduces_to_forward():
+    """A full cache with as many queries as rows is ordinary (causal) attention."""
+    out = []
+    r = _rng(24)
+    for causal in (False, True):
+        q, k, v = (r.standard_normal((2, 2, 6, 4)) for _ in range(3))
+        o, lse = A.attention_decode(q, k, v, None, causal, 0.5)
+        of, lf = A.attention_forward(q, k, v, causal, 0.5)
+        err = max(_maxdiff(o, of), _maxdiff(lse, lf))
+        _fail_if(not err <= 1e-14, f"decode with Nq = Nk != forward (causal={causal}): {err:.3e}", out)
+    return out
+
+
 # --------------------------------------------------------------------------- library routines
 
 def pin_torch_float64():
@@ -411,6 +468,8 @@ ALL_PINS = [
     pin_row_chunking,
     pin_gqa_brute_force,
     pin_gqa_finite_differences,
+    pin_decode_brute_force,
+    pin_decode_reduces_to_forward,
 ]
 
 

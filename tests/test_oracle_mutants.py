@@ -113,6 +113,14 @@ def m_group_mean(g, hkv):
     return g.reshape(B, hkv, hq // hkv, n, d).mean(axis=2)
 
 
+def m_decode_top_left(length, nq):
+    return np.arange(int(nq))  # queries aligned to the start of the cache
+
+
+def m_decode_off_by_one(length, nq):
+    return int(length) - int(nq) + 1 + np.arange(int(nq))
+
+
 MUTANTS = [
     ("scores", m_no_scale),
     ("scores", m_transposed_scores),
@@ -130,6 +138,8 @@ MUTANTS = [
     ("kv_head", m_kv_head_modulo),
     ("group_sum", m_group_first),
     ("group_sum", m_group_mean),
+    ("decode_positions", m_decode_top_left),
+    ("decode_positions", m_decode_off_by_one),
 ]
 
 
