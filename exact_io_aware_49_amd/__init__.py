@@ -8,11 +8,14 @@ from .fa import (  # noqa: F401
     FA_DTYPE_F32,
     LIB_PATH,
     backward,
+    decode,
     default_scale,
     fa_bwd,
     fa_bwd_gqa,
     fa_bwd_gqa_workspace_size,
     fa_bwd_workspace_size,
+    fa_decode,
+    fa_decode_workspace_size,
     fa_fwd,
     fa_fwd_gqa,
     fa_status_string,

@@ -43,6 +43,24 @@ int check_heads(int Hq, int Hkv) {
   return FA_OK;
 }
 
+// Decode: Nq query rows of B*Hq heads against a [B, Hkv, Nk, d] cache
+int check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale, int dtype) {
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+  if (B < 1 || Nq < 1 || Nk < 1) return FA_ERR_BAD_SHAPE;
+  if (check_heads(Hq, Hkv) != FA_OK) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+  const unsigned long long lim = 1ull << 55;
+  if ((unsigned long long)B * (unsigned long long)Hkv > lim / (unsigned long long)Nk) return FA_ERR_BAD_SHAPE;
+  if ((unsigned long long)B * (unsigned long long)Hq > lim / (unsigned long long)Nq) return FA_ERR_BAD_SHAPE;
+  if ((unsigned long long)Nk * (unsigned long long)d * 2ull >= (1ull << 31)) return FA_ERR_BAD_SHAPE;
+  if ((unsigned long long)Hq / Hkv * (unsigned long long)Nq > 0x7fffffffull) return FA_ERR_BAD_SHAPE;
+  const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d);
+  if ((p.nwaves + 3) / 4 > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_BAD_ARGUMENT;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_SCALE;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +147,27 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            int causal, float scale, int dtype, void *stream) {
   return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d, causal, scale,
                     dtype, stream);
+}
+
+size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype) {
+  if (check_decode(B, Hq, Hkv, Nq, Nk, d, 0, 1.0f, dtype) != FA_OK) return 0;
+  return fa::decode_plan(B, Hq, Hkv, Nq, Nk, d).bytes;
+}
+
+int fa_decode(const void *q, const void *k, const void *v, const int *kv_lens, void *o, float *lse, void *workspace,
+              size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+              int dtype, void *stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+  int st = check_decode(B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  const size_t need = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d).bytes;
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(kv_lens) & 3u) != 0)
+    return FA_ERR_MISALIGNED;
+  hipError_t e = fa::launch_decode_bf16(q, k, v, kv_lens, o, lse, (float *)workspace, B, Hq, Hkv, Nq, Nk, d,
+                                        causal == 1, scale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

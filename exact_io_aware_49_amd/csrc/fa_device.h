@@ -208,6 +208,20 @@ __device__ __forceinline__ int swz_rt(int r) {
   return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
+// Chunk permutations of a streamed K or V tile (physical chunk = logical
+// chunk ^ swz(row)).  swz_k makes the score reads (16 consecutive rows, one
+// 16-byte chunk each) hit distinct banks; swz_v does the same for the
+// transposed value reads (4 rows x 4 chunks per 16 lanes).  At d >= 128 a row
+// is a multiple of the 256-byte bank cycle, so d = 128 and d = 256 share them.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return (D >= 128) ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return (D >= 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)FA_LDS(const void, p);

@@ -64,15 +64,6 @@ struct FwdCfg {
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 };
 
-// Chunk permutations (physical chunk = logical chunk ^ swz(row)).
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  return (D >= 128) ? (r & 15) : ((r >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-  return (D >= 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
-}
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, (D == 256) ? 1 : 2)

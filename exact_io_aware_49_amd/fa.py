@@ -61,6 +61,10 @@ def load_library(path: str = LIB_PATH):
     lib.fa_bwd_gqa_workspace_size.restype = sz
     lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_gqa.restype = i
+    lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_decode_workspace_size.restype = sz
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_decode.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -97,6 +101,16 @@ def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
                dtype, stream) -> int:
     return load_library().fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
                                      N, d, causal, scale, dtype, stream)
+
+
+def fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, dtype) -> int:
+    return load_library().fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, dtype)
+
+
+def fa_decode(q, k, v, kv_lens, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype,
+              stream) -> int:
+    return load_library().fa_decode(q, k, v, kv_lens, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
+                                    causal, scale, dtype, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -196,3 +210,37 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
                       B, H, hkv, N, d, int(bool(causal)), scale, code, _stream_handle(q.device)))
     return dq, dk, dv
+
+
+def decode(q, k, v, kv_lens=None, causal: bool = False, scale: float | None = None, workspace=None):
+    """Attention of Nq new query rows against a key/value cache (bf16).
+
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d] (cache capacity Nk, Hkv dividing Hq);
+    kv_lens: int32 [B] device tensor of valid cache rows per sequence, or None (all Nk).
+    Query i of sequence b sits at position kv_lens[b] - Nq + i.  Returns (o like q,
+    lse float32 [B, Hq, Nq]).
+    """
+    load_library()
+    _check_tensors(q, k, v)
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise RuntimeError("decode takes bfloat16 q, k, v")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise RuntimeError("q must be [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d]")
+    B, H, nq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    lens_ptr = 0
+    if kv_lens is not None:
+        _check_tensors(q, kv_lens)
+        if kv_lens.dtype != torch.int32 or kv_lens.shape != (B,):
+            raise RuntimeError("kv_lens must be an int32 tensor of shape [B]")
+        lens_ptr = kv_lens.data_ptr()
+    scale = default_scale(d) if scale is None else float(scale)
+    need = fa_decode_workspace_size(B, H, hkv, nq, nk, d, FA_DTYPE_BF16)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device=q.device)
+    _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), lens_ptr or None, o.data_ptr(), lse.data_ptr(),
+                     workspace.data_ptr(), workspace.numel(), B, H, hkv, nq, nk, d, int(bool(causal)), scale,
+                     FA_DTYPE_BF16, _stream_handle(q.device)))
+    return o, lse

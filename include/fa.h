@@ -150,6 +150,34 @@ FA_API int fa_bwd_gqa(const void *q, const void *k, const void *v, const void *o
                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                int dtype, void *stream);
 
+/*
+ * Attention of a few new query rows against a key/value cache (decode), the
+ * serving case "FlashAttention (DE)", section "Evolution und
+ * Weiterentwicklungen", subsection "Spezialisierte Lösungen" names
+ * (FlashInfer: the KV cache in streaming generation).
+ *
+ *   q       : [B,Hq,Nq,d] bf16, the Nq newest positions of each sequence.
+ *   k, v    : [B,Hkv,Nk,d] bf16 cache; Nk is its capacity.  Query heads share
+ *             K/V heads as in fa_fwd_gqa (Hkv divides Hq).
+ *   kv_lens : device int32 [B], the valid cache rows L_b of each sequence, or
+ *             NULL for L_b = Nk.  Values are clamped to [0, Nk].
+ *   o       : [B,Hq,Nq,d] bf16 output;  lse : [B,Hq,Nq] float32 output.
+ * Query i of sequence b sits at position L_b - Nq + i.  It attends to cache
+ * rows j < L_b; with causal = 1 only to j <= L_b - Nq + i.  A query that sees
+ * no row gets o = 0 and lse = -inf.
+ * Only FA_DTYPE_BF16 and d in {64, 128}.  The workspace (at least
+ * fa_decode_workspace_size() bytes, 16-byte aligned) holds float32 partial
+ * results: the cache is split into key ranges over many waves so that K and V
+ * stream from HBM once at full bandwidth, and a second kernel merges the
+ * ranges (lse = ln sum_s e^lse_s, o = sum_s e^(lse_s - lse) o_s).
+ * fa_decode_workspace_size returns 0 for arguments fa_decode would reject.
+ */
+FA_API size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype);
+FA_API int fa_decode(const void *q, const void *k, const void *v, const int *kv_lens,
+              void *o, float *lse, void *workspace, size_t workspace_bytes,
+              int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+              int dtype, void *stream);
+
 /* A static, human-readable string for a status code (never NULL). */
 FA_API const char *fa_status_string(int status);
 

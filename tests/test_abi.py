@@ -28,7 +28,8 @@ def test_library_exports_every_declared_symbol():
     lib = fa.load_library()
     names = declared_symbols()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_gqa", "fa_bwd_gqa",
-                          "fa_bwd_gqa_workspace_size", "fa_status_string", "fa_version"}
+                          "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size",
+                          "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(lib, n), n
     raw = ctypes.CDLL(fa.LIB_PATH)
@@ -129,6 +130,37 @@ def test_gqa_workspace_size():
     assert fa.fa_bwd_gqa_workspace_size(8, 64, 8, 4096, 128, 1) == 2 * 8 * 64 * 4096 * 4   # enough key blocks: no split
     assert fa.fa_bwd_gqa_workspace_size(2, 32, 5, 2048, 128, 1) == 0
     assert fa.fa_bwd_gqa_workspace_size(2, 32, 32, 2048, 128, 1) == fa.fa_bwd_workspace_size(2, 32, 2048, 128, 1)
+
+
+def dec(**kw):
+    a = dict(q=P, k=P, v=P, lens=None, o=P, lse=P, ws=P, wsb=1 << 30, B=2, Hq=8, Hkv=2, Nq=1, Nk=4096, d=128,
+             causal=0, scale=0.125, dtype=1, stream=None)
+    a.update(kw)
+    return fa.fa_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["ws"], a["wsb"], a["B"], a["Hq"],
+                        a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(lse=None), 1),
+    (dict(B=0), 2), (dict(Nq=0), 2), (dict(Nk=0), 2), (dict(Hkv=3), 2), (dict(Hkv=0), 2),
+    (dict(Nk=1 << 23), 2), (dict(d=256), 3), (dict(d=96), 3), (dict(dtype=0), 4),
+    (dict(scale=0.0), 5), (dict(scale=float("nan")), 5), (dict(q=P + 8), 6), (dict(lens=P + 2), 6),
+    (dict(ws=P + 4), 6), (dict(ws=None), 7), (dict(wsb=1024), 7), (dict(causal=2), 8),
+])
+def test_decode_validation(kw, code):
+    assert dec(**kw) == code
+
+
+def test_decode_workspace_size():
+    # float32 partial O and lse per (query row, key range), 256-byte aligned
+    n = fa.fa_decode_workspace_size(16, 32, 8, 1, 8192, 128, 1)
+    rows = 16 * 32 * 1
+    assert n > 0 and n % 256 == 0
+    splits = (n - 256) // (rows * (128 + 1) * 4)
+    assert splits >= 1 and n >= rows * splits * (128 + 1) * 4
+    assert fa.fa_decode_workspace_size(16, 32, 8, 1, 8192, 128, 0) == 0
+    assert fa.fa_decode_workspace_size(16, 32, 7, 1, 8192, 128, 1) == 0
+    assert fa.fa_decode_workspace_size(1, 1, 1, 1, 1, 64, 1) >= 64 * 4 + 4
 
 
 def test_workspace_size():

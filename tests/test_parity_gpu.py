@@ -133,6 +133,52 @@ def test_bwd_encoder_shape():
     check_bwd_heads(q, k, v, do, False, w.scale, [(0, 0), (3, 15)], "bwd_encoder_b4h16n4096d128")
 
 
+# ------------------------------------------------------------------ decode (key/value cache)
+
+def _decode_check(q, k, v, lens, causal, tag):
+    """fa.decode against the oracle on every output.  Rows that see no cache row must be
+    exactly O = 0, lse = -inf; the rest use the bf16 bounds."""
+    d = q.shape[3]
+    say(f"[decode] {tag} q={q.shape} cache={k.shape} causal={causal} lens={None if lens is None else lens.tolist()[:8]}")
+    ld = None if lens is None else torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to("cuda")
+    o, lse = fa.decode(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), ld, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    ro, rl = oracle.attention_decode(q, k, v, lens, causal, f32(d ** -0.5))
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), empty), f"{tag}: rows without visible keys differ"
+    assert np.all(o[empty] == 0.0), f"{tag}: a row without visible keys has O != 0"
+    eo = assert_close(f"{tag} O", o, ro, "bf16")
+    if (~empty).any():
+        el = assert_close(f"{tag} lse", lse[~empty], rl[~empty], "bf16", lse=True)
+        say(f"   O max/rel {eo[0]:.2e}/{eo[1]:.2e}  lse max {el[0]:.2e}  empty rows {int(empty.sum())}")
+
+
+@pytest.mark.parametrize("name", list(inputs.DECODE_CASES))
+def test_decode_cases(name):
+    need_gpu()
+    c = inputs.DECODE_CASES[name]
+    q, k, v, lens = inputs.gen_decode(c["B"], c["hq"], c["hkv"], c["nq"], c["nk"], c["d"], c["seed"], c["min_len"])
+    _decode_check(q, k, v, lens, c["causal"], name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_sweep(d, causal):
+    """Ragged cache lengths (including 0 and fewer rows than queries), 1..40 query rows,
+    shared K/V heads, caches that end inside a tile."""
+    need_gpu()
+    for i, (hq, hkv, nq, nk) in enumerate([(1, 1, 1, 1), (4, 2, 1, 33), (4, 2, 3, 300), (2, 1, 40, 1000),
+                                            (8, 8, 2, 70), (6, 2, 17, 513)]):
+        rng = np.random.Generator(np.random.PCG64(1400 + i + d))
+        lens = rng.integers(0, nk + 1, size=3).astype(np.int32)
+        lens[0] = nk
+        q, k, v, _ = inputs.gen_decode(3, hq, hkv, nq, nk, d, 1500 + 7 * i + d)
+        _decode_check(q, k, v, lens, causal, f"decode sweep Hq={hq} Hkv={hkv} Nq={nq} Nk={nk}")
+    q, k, v, _ = inputs.gen_decode(2, 2, 1, 5, 200, d, 1600 + d)
+    _decode_check(q, k, v, None, causal, "decode full cache")
+
+
 # ------------------------------------------------------------------ head dim 256 (forward)
 
 @pytest.mark.parametrize("causal", [False, True])
