@@ -4,7 +4,9 @@
 
 --workload also accepts the shared-K/V-head cases (query heads grouped over
 fewer K/V heads), e.g. gqa_causal_b2hq32hkv4n2048d128; they are timed the same
-way through fa_fwd_gqa / fa_bwd_gqa.
+way through fa_fwd_gqa / fa_bwd_gqa.  The decode cases (new query rows against
+a key/value cache, e.g. decode_b16hq32hkv8nk8192d128) time one fa_decode call
+per step and report the K/V streaming rate in GB/s against the 8 TB/s HBM peak.
 
 A step runs the whole path once over one batch of synthetic inputs that are
 already resident in device memory: fa_fwd (O, lse) then fa_bwd (dQ, dK, dV,
@@ -134,6 +136,90 @@ class _Case:
         return inputs.gen_gqa(self.B, self.H, self.hkv, self.N, self.d, "bf16", self.seed, with_do=True)
 
 
+def decode_main(a, name):
+    """One fa_decode call per step; value = K/V bytes of the valid cache rows / time."""
+    import torch
+
+    import exact_io_aware_49_amd as fa
+    from exact_io_aware_49_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    fa.load_library()
+    c = inputs.DECODE_CASES[name]
+    B, hq, hkv, nq, nk, d = c["B"], c["hq"], c["hkv"], c["nq"], c["nk"], c["d"]
+    q, k, v, lens = inputs.gen_decode(B, hq, hkv, nq, nk, d, c["seed"], c["min_len"])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
+    ld = torch.from_numpy(lens).to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, hq, nq), dtype=torch.float32, device=dev)
+    wsb = fa.fa_decode_workspace_size(B, hq, hkv, nq, nk, d, fa.FA_DTYPE_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    scale = d ** -0.5
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        rc = fa.fa_decode(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), ld.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          ws.data_ptr(), wsb, B, hq, hkv, nq, nk, d, int(c["causal"]), scale, fa.FA_DTYPE_BF16,
+                          stream.cuda_stream)
+        if rc:
+            raise RuntimeError(fa.fa_status_string(rc))
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_per_step = wall * 1e3 / a.steps
+    kv_bytes = 2.0 * hkv * float(lens.astype(np.int64).sum()) * d * 2
+    io_bytes = kv_bytes + 2.0 * B * hq * nq * d * 2 + B * hq * nq * 4  # + Q read, O and lse written
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = io_bytes / (launch_ms * 1e-3) / 1e9
+    line = {
+        "metric": "decode K/V streaming GB/s on 1 MI355X + % of 8 TB/s HBM",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: i.i.d. N(0,1) from PCG64, rounded to bf16, resident in HBM; cache lengths seeded",
+        "config": {"workload": name, "B": B, "Hq": hq, "Hkv": hkv, "Nq": nq, "Nk": nk, "d": d,
+                   "causal": bool(c["causal"]), "cache_rows": int(lens.sum())},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "fa_decode (fa_decode_kernel + fa_decode_merge_kernel)",
+                     "avg_launch_ms": round(launch_ms, 4)},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        done = 0
+        rows = 0
+        for b in range(B):
+            oracle.attention_decode(q[b:b + 1], k[b:b + 1], v[b:b + 1], lens[b:b + 1], c["causal"],
+                                    float(np.float32(scale)))
+            done += 1
+            rows += int(lens[b])
+            if time.perf_counter() - t0 >= a.cpu_budget:
+                break
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(2.0 * hkv * rows * d * 2 / dt / 1e9, 3), "unit": "GB/s",
+                                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                "sample": f"{done} of {B} sequences, float64 numpy, {dt:.1f} s wall"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +236,10 @@ def main(argv=None):
               "independent, so a multi-GPU run would shard heads with no communication). Use --gpus 1.",
               file=sys.stderr)
         return 2
+
+    from exact_io_aware_49_amd import inputs as _inputs
+    if a.workload in _inputs.DECODE_CASES:
+        return decode_main(a, a.workload)
 
     import torch
 

@@ -56,6 +56,7 @@ int check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, floa
   if ((unsigned long long)Hq / Hkv * (unsigned long long)Nq > 0x7fffffffull) return FA_ERR_BAD_SHAPE;
   const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d);
   if ((p.nwaves + 3) / 4 > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
+  if ((long long)B * Hq * Nq > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;  // one merge workgroup per query row
   if (causal != 0 && causal != 1) return FA_ERR_BAD_ARGUMENT;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_SCALE;
   return FA_OK;

@@ -16,7 +16,7 @@
 // and V tiles into its own double-buffered LDS area with buffer_load ... lds,
 // computes S^T = K Q^T and O^T += V^T P^T on bf16 matrix cores exactly as the
 // forward does, and writes a float32 (O, lse) partial for its key range.
-// fa_decode_merge_kernel: one thread per 8 output columns of a query row.
+// fa_decode_merge_kernel: one workgroup per query row.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -222,34 +222,71 @@ fa_decode_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
 
 // Merge the nsplit partials of each query row: lse = m + ln sum_s e^(lse_s - m),
 // O = sum_s e^(lse_s - lse) O_s.  A row no split saw gets O = 0, lse = -inf.
+// One workgroup per row: the weights go through LDS, then each thread sums
+// 8 columns over a strided subset of the splits and the subsets are added in
+// a fixed order, so the result is bitwise reproducible.
 template <int D>
 __global__ void __launch_bounds__(256)
 fa_decode_merge_kernel(const float *__restrict__ Opart, const float *__restrict__ Lpart, __bf16 *__restrict__ O,
-                       float *__restrict__ LSE, long long nrows, int nsplit) {
-  constexpr int C8 = D / 8;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = idx / C8;
-  const int c8 = (int)(idx - row * C8);
-  if (row >= nrows) return;
+                       float *__restrict__ LSE, int nsplit) {
+  constexpr int C8 = D / 8;          // 8-column chunks per row
+  constexpr int SG = 256 / C8;       // split groups
+  __shared__ float red[256];
+  __shared__ floatx4 part[SG][C8][2];
+  const int tid = threadIdx.x;
+  const long long row = blockIdx.x;
   const float *lp = Lpart + row * nsplit;
+  // ---- maximum and sum of e^(lse_s - m) over the splits
   float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lp[s]);
-  floatx4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+  for (int s = tid; s < nsplit; s += 256) m = fmaxf(m, lp[s]);
+  red[tid] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  m = red[0];
+  __syncthreads();
   float sum = 0.f;
+  if (m != -INFINITY)
+    for (int s = tid; s < nsplit; s += 256) sum += expf(lp[s] - m);
+  red[tid] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  sum = red[0];
+  // ---- weighted sum of the partial rows
+  const int c8 = tid % C8;
+  const int sg = tid / C8;
+  floatx4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
   if (m != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
+    for (int s = sg; s < nsplit; s += SG) {
       const float w = expf(lp[s] - m);
-      sum += w;
       const float *op = Opart + (row * nsplit + s) * D + 8 * c8;
       a += w * *reinterpret_cast<const floatx4 *>(op);
       b += w * *reinterpret_cast<const floatx4 *>(op + 4);
     }
-    a /= sum;
-    b /= sum;
   }
-  const u32x4 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
-  *reinterpret_cast<u32x4 *>(O + row * D + 8 * c8) = w;
-  if (c8 == 0) LSE[row] = (m == -INFINITY) ? -INFINITY : m + logf(sum);
+  part[sg][c8][0] = a;
+  part[sg][c8][1] = b;
+  __syncthreads();
+  if (tid < C8) {
+    floatx4 ta = {0, 0, 0, 0}, tb = {0, 0, 0, 0};
+    for (int g = 0; g < SG; ++g) {
+      ta += part[g][tid][0];
+      tb += part[g][tid][1];
+    }
+    if (m != -INFINITY) {
+      ta /= sum;
+      tb /= sum;
+    }
+    const u32x4 w = {pack_bf16x2(ta[0], ta[1]), pack_bf16x2(ta[2], ta[3]), pack_bf16x2(tb[0], tb[1]),
+                     pack_bf16x2(tb[2], tb[3])};
+    *reinterpret_cast<u32x4 *>(O + row * D + 8 * tid) = w;
+    if (tid == 0) LSE[row] = (m == -INFINITY) ? -INFINITY : m + logf(sum);
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -266,9 +303,9 @@ hipError_t launch(const void *q, const void *k, const void *v, const int *kv_len
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nrows = (long long)B * Hq * Nq;
-  const long long threads = nrows * (D / 8);
-  hipLaunchKernelGGL((fa_decode_merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                     (const float *)opart, (const float *)lpart, (__bf16 *)o, lse, nrows, p.nsplit);
+  if (nrows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa_decode_merge_kernel<D>), dim3((unsigned)nrows), dim3(256), 0, stream,
+                     (const float *)opart, (const float *)lpart, (__bf16 *)o, lse, p.nsplit);
   return hipGetLastError();
 }
 
