@@ -80,6 +80,42 @@ def bf16_bits(x_bf16_valued: np.ndarray) -> np.ndarray:
     return (u >> np.uint32(16)).astype(np.uint16)
 
 
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP E4M3 codes (uint8), round to nearest even, saturating at +-448.
+
+    Used only to make FP8 test inputs: a value is first rounded to the E4M3 grid
+    (3 mantissa bits for normals, steps of 2^-9 below 2^-6) and then encoded.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.minimum(np.abs(x), 448.0)
+    # exponent of the grid step: normals have step 2^(e-3), subnormals 2^-9
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    step = np.exp2(e - 3.0)
+    q = np.round(a / step) * step            # numpy rounds halves to even
+    q = np.minimum(q, 448.0)
+    e2 = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+    normal = q >= 2.0 ** -6
+    mant = np.where(normal, np.round((q / np.exp2(e2) - 1.0) * 8.0), np.round(q / 2.0 ** -9))
+    exp_field = np.where(normal, e2 + 7.0, 0.0)
+    code = (exp_field.astype(np.int64) << 3) | mant.astype(np.int64)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def gen_fp8(shape, seed: int):
+    """Q, K, V as E4M3 codes with per-tensor scales: N(0,1) float32 (PCG64, Q, K, V in
+    that order), each divided by scale = max|x| / 448 and encoded.  Returns
+    ([q8, k8, v8], [q_scale, k_scale, v_scale])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    codes, scales = [], []
+    for _ in range(3):
+        a = rng.standard_normal(size=tuple(shape), dtype=np.float32)
+        sc = float(np.float32(np.abs(a).max() / 448.0))
+        codes.append(e4m3_encode(a / sc))
+        scales.append(sc)
+    return codes, scales
+
+
 def gen_tensors(shape, dtype: str, seed: int, count: int):
     """`count` arrays of `shape`, i.i.d. N(0,1) float32 from PCG64(seed), in draw order.
 

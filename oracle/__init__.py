@@ -33,4 +33,6 @@ from .attention import (  # noqa: F401
     group_sum,
     decode_positions,
     attention_decode,
+    e4m3_to_float,
+    attention_forward_fp8,
 )

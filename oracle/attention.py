@@ -287,3 +287,35 @@ def attention_decode(q, k, v, kv_lens, causal: bool, scale: float):
             o[b, h] = p @ np.asarray(v[b, hk, :length], dtype=np.float64)
             lse[b, h] = _lse(m, l)
     return o, lse
+
+
+def e4m3_to_float(codes) -> np.ndarray:
+    """Decode 8-bit floating point codes in the OCP E4M3 format to float64.
+
+    FP8 inputs are named for FlashAttention-3 in "FlashAttention (DE)",
+    section "Evolution und Weiterentwicklungen", subsection
+    "FlashAttention-3 (2024)"; the pages do not fix a format.  The reading
+    here is the OCP 8-bit floating point E4M3 format: sign bit, 4 exponent
+    bits with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
+    m * 2^-9; there are no infinities; S.1111.111 is NaN; the largest finite
+    magnitude is 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def attention_forward_fp8(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float, causal: bool,
+                          scale: float):
+    """Exact attention of FP8 inputs: the real inputs are the decoded E4M3 codes times their
+    per-tensor scale factors (Q = e4m3(q8) * q_scale, and so on); the rest is attention_forward.
+    Returns (O, lse) float64.
+    """
+    q = e4m3_to_float(q8) * float(q_scale)
+    k = e4m3_to_float(k8) * float(k_scale)
+    v = e4m3_to_float(v8) * float(v_scale)
+    return attention_forward(q, k, v, causal, scale)

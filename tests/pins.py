@@ -384,6 +384,46 @@ def pin_decode_reduces_to_forward():
     return out
 
 
+# --------------------------------------------------------------------------- FP8 inputs
+
+def pin_e4m3_codes():
+    """Values of the OCP E4M3 format (bias 7, 3 mantissa bits, subnormal step 2^-9, largest
+    finite 448, S.1111.111 NaN, no infinities), code by code."""
+    out = []
+    table = {0x00: 0.0, 0x38: 1.0, 0xB8: -1.0, 0x40: 2.0, 0x3C: 1.5, 0x30: 0.5, 0x08: 2.0 ** -6,
+             0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x0F: 1.875 * 2.0 ** -6, 0x7E: 448.0, 0xFE: -448.0,
+             0x77: 240.0, 0x78: 256.0, 0x4E: 7.0}
+    dec = A.e4m3_to_float(np.array(list(table), dtype=np.uint8))
+    for (code, want), got in zip(table.items(), dec):
+        _fail_if(not got == want, f"e4m3 code 0x{code:02x}: {got} != {want}", out)
+    _fail_if(not np.isnan(A.e4m3_to_float(np.array([0x7F, 0xFF], np.uint8))).all(), "e4m3 NaN codes", out)
+    allv = A.e4m3_to_float(np.arange(0x00, 0x7F, dtype=np.uint8))
+    _fail_if(not np.all(np.diff(allv) > 0), "e4m3 positive codes not strictly increasing", out)
+    # spacing: 2^-9 among the subnormals and in the first binade, doubling with each binade
+    d = np.diff(allv)
+    want = np.array([2.0 ** -9 if i < 8 else 2.0 ** ((i >> 3) - 10) for i in range(len(d))])
+    _fail_if(not np.allclose(d, want, rtol=0, atol=0), "e4m3 spacing", out)
+    return out
+
+
+def pin_fp8_forward_is_forward_of_decoded():
+    """The FP8 forward equals the plain forward of the decoded, scaled inputs (brute force)."""
+    out = []
+    r = _rng(25)
+    codes = [r.integers(0, 0x7F, size=(1, 1, 5, 3)).astype(np.uint8) | (r.integers(0, 2, size=(1, 1, 5, 3)).astype(np.uint8) << 7) for _ in range(3)]
+    scales = [0.01, 0.02, 0.5]
+    o, lse = A.attention_forward_fp8(*codes, *scales, True, 0.7)
+    vals = []
+    for c, sc in zip(codes, scales):
+        vals.append([[math.copysign(1.0, -1.0 if (x & 0x80) else 1.0) *
+                      ((x & 7) * 2.0 ** -9 if ((x >> 3) & 15) == 0 else (1 + (x & 7) / 8) * 2.0 ** (((x >> 3) & 15) - 7)) * sc
+                      for x in row] for row in c[0, 0].tolist()])
+    bo, bl = brute_forward(vals[0], vals[1], vals[2], True, 0.7)
+    err = max(_maxdiff(o[0, 0], bo), _maxdiff(lse[0, 0], bl))
+    _fail_if(not err <= 1e-14, f"fp8 forward vs brute force: {err:.3e}", out)
+    return out
+
+
 # --------------------------------------------------------------------------- library routines
 
 def pin_torch_float64():
@@ -470,6 +510,8 @@ ALL_PINS = [
     pin_gqa_finite_differences,
     pin_decode_brute_force,
     pin_decode_reduces_to_forward,
+    pin_e4m3_codes,
+    pin_fp8_forward_is_forward_of_decoded,
 ]
 
 

@@ -60,3 +60,21 @@ def test_workload_table():
     assert enc.shape == (4, 16, 4096, 128) and not enc.causal and enc.dtype == "bf16"
     assert abs(enc.scale - 128 ** -0.5) < 1e-15
     assert w["bwd_causal_b4h16n2048d64"].kind == "bwd"
+
+
+def test_e4m3_encoder_round_trip():
+    """The FP8 input encoder hits every finite E4M3 code exactly and rounds to the nearest
+    grid value (ties to even) otherwise."""
+    import oracle
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.e4m3_to_float(codes)
+    back = inputs.e4m3_encode(vals.astype(np.float32))
+    same = (back == codes) | ((codes == 0x80) & (back == 0x00))  # -0 may encode as +0
+    assert same.all()
+    rng = np.random.Generator(np.random.PCG64(7))
+    x = (rng.standard_normal(10000) * 50).astype(np.float32)
+    q = oracle.e4m3_to_float(inputs.e4m3_encode(x))
+    grid = np.sort(oracle.e4m3_to_float(np.arange(0, 0x7F, dtype=np.uint8)))
+    for xv, qv in zip(np.abs(x[:500]), np.abs(q[:500])):
+        best = grid[np.argmin(np.abs(grid - min(xv, 448.0)))]
+        assert abs(min(xv, 448.0) - qv) <= abs(min(xv, 448.0) - best) + 1e-12

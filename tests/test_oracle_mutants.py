@@ -121,6 +121,19 @@ def m_decode_off_by_one(length, nq):
     return int(length) - int(nq) + 1 + np.arange(int(nq))
 
 
+_orig_e4m3 = A.e4m3_to_float
+
+
+def m_e4m3_bias8(codes):
+    return _orig_e4m3(codes) / 2.0  # exponent bias 8 instead of 7
+
+
+def m_e4m3_no_subnormals(codes):
+    c = np.asarray(codes, np.uint8)
+    v = _orig_e4m3(c)
+    return np.where(((c >> 3) & 15) == 0, 0.0, v)
+
+
 MUTANTS = [
     ("scores", m_no_scale),
     ("scores", m_transposed_scores),
@@ -140,6 +153,8 @@ MUTANTS = [
     ("group_sum", m_group_mean),
     ("decode_positions", m_decode_top_left),
     ("decode_positions", m_decode_off_by_one),
+    ("e4m3_to_float", m_e4m3_bias8),
+    ("e4m3_to_float", m_e4m3_no_subnormals),
 ]
 
 
