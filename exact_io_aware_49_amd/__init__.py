@@ -17,9 +17,11 @@ from .fa import (  # noqa: F401
     fa_decode,
     fa_decode_workspace_size,
     fa_fwd,
+    fa_fwd_fp8,
     fa_fwd_gqa,
     fa_status_string,
     fa_version,
     forward,
+    forward_fp8,
     load_library,
 )

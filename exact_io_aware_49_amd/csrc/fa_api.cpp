@@ -106,6 +106,24 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
   return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
 }
 
+int fa_fwd_fp8(const void *q, const void *k, const void *v, float q_scale, float k_scale, float v_scale, void *o,
+               float *lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale, void *stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
+  int st = check_common(B, Hq, N, d, causal, scale, FA_DTYPE_BF16, true);
+  if (st == FA_OK) st = check_heads(Hq, Hkv);
+  if (st != FA_OK) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+  for (float x : {q_scale, k_scale, v_scale})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_BAD_SCALE;
+  const float c = q_scale * k_scale * scale;
+  if (!std::isnormal(c) || !std::isnormal(c * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_MISALIGNED;
+  hipError_t e = fa::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hq / Hkv, N, d, causal == 1,
+                                    scale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_gqa_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype) {
   if (check_common(B, Hq, N, d, 0, 1.0f, dtype, false) != FA_OK || check_heads(Hq, Hkv) != FA_OK ||
       dtype != FA_DTYPE_BF16)

@@ -65,6 +65,8 @@ def load_library(path: str = LIB_PATH):
     lib.fa_decode_workspace_size.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_decode.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -111,6 +113,11 @@ def fa_decode(q, k, v, kv_lens, o, lse, workspace, workspace_bytes, B, Hq, Hkv, 
               stream) -> int:
     return load_library().fa_decode(q, k, v, kv_lens, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
                                     causal, scale, dtype, stream)
+
+
+def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale, stream) -> int:
+    return load_library().fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                                     stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -243,4 +250,30 @@ def decode(q, k, v, kv_lens=None, causal: bool = False, scale: float | None = No
     _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), lens_ptr or None, o.data_ptr(), lse.data_ptr(),
                      workspace.data_ptr(), workspace.numel(), B, H, hkv, nq, nk, d, int(bool(causal)), scale,
                      FA_DTYPE_BF16, _stream_handle(q.device)))
+    return o, lse
+
+
+def forward_fp8(q, k, v, q_scale: float, k_scale: float, v_scale: float, causal: bool = False,
+                scale: float | None = None):
+    """Exact attention forward on FP8 (E4M3) inputs.
+
+    q: [B, Hq, N, d], k, v: [B, Hkv, N, d] uint8 tensors of E4M3 codes (or torch.float8_e4m3fn,
+    viewed as bytes); the value of a code is e4m3(code) * its tensor's scale.  Returns (o bf16
+    [B, Hq, N, d], lse float32 [B, Hq, N]).
+    """
+    load_library()
+    q, k, v = (t.view(torch.uint8) if t.dtype != torch.uint8 else t for t in (q, k, v))
+    _check_tensors(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise RuntimeError("q must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    hkv = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d) or hkv < 1 or H % hkv != 0:
+        raise RuntimeError("k, v must be [B, Hkv, N, d] with Hkv dividing the query head count")
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(q_scale), float(k_scale), float(v_scale),
+                      o.data_ptr(), lse.data_ptr(), B, H, hkv, N, d, int(bool(causal)), scale,
+                      _stream_handle(q.device)))
     return o, lse

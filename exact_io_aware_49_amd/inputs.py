@@ -102,14 +102,15 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return (code.astype(np.uint8) | sign).astype(np.uint8)
 
 
-def gen_fp8(shape, seed: int):
+def gen_fp8(shape, seed: int, kv_shape=None):
     """Q, K, V as E4M3 codes with per-tensor scales: N(0,1) float32 (PCG64, Q, K, V in
-    that order), each divided by scale = max|x| / 448 and encoded.  Returns
-    ([q8, k8, v8], [q_scale, k_scale, v_scale])."""
+    that order; K and V of kv_shape when given), each divided by scale = max|x| / 448 and
+    encoded.  Returns ([q8, k8, v8], [q_scale, k_scale, v_scale])."""
     rng = np.random.Generator(np.random.PCG64(seed))
     codes, scales = [], []
-    for _ in range(3):
-        a = rng.standard_normal(size=tuple(shape), dtype=np.float32)
+    kv_shape = shape if kv_shape is None else kv_shape
+    for shp in (shape, kv_shape, kv_shape):
+        a = rng.standard_normal(size=tuple(shp), dtype=np.float32)
         sc = float(np.float32(np.abs(a).max() / 448.0))
         codes.append(e4m3_encode(a / sc))
         scales.append(sc)
@@ -186,6 +187,19 @@ DECODE_CASES = {
     "decode_spec4_causal_b8hq16hkv16nk4096d64": dict(B=8, hq=16, hkv=16, nq=4, nk=4096, d=64, causal=True,
                                                      min_len=None, seed=52),
 }
+
+
+# FP8 (E4M3) forward shapes: the 16-head, 4K-token, head-dim-128 encoder layer
+# at batch 4 (16K tokens per batch), and a causal grouped-query decoder layer
+# (32 query heads over 8 K/V heads, head dim 64, 2K tokens).
+FP8_CASES = {
+    "fp8_fwd_b4h16n4096d128": dict(B=4, hq=16, hkv=16, N=4096, d=128, causal=False, seed=61),
+    "fp8_fwd_gqa_causal_b2hq32hkv8n2048d64": dict(B=2, hq=32, hkv=8, N=2048, d=64, causal=True, seed=62),
+}
+
+
+def fp8_case_inputs(c: dict):
+    return gen_fp8((c["B"], c["hq"], c["N"], c["d"]), c["seed"], (c["B"], c["hkv"], c["N"], c["d"]))
 
 
 def workload_inputs(w: Workload):

@@ -178,6 +178,32 @@ FA_API int fa_decode(const void *q, const void *k, const void *v, const int *kv_
               int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
               int dtype, void *stream);
 
+/*
+ * Forward with FP8 inputs, the low-precision mode of FlashAttention-3
+ * ("FlashAttention (DE)", section "Evolution und Weiterentwicklungen",
+ * subsection "FlashAttention-3 (2024)").
+ *
+ *   q : [B,Hq,N,d], k, v : [B,Hkv,N,d]  one byte per element, OCP FP8 E4M3
+ *       codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ *       infinities; 0x7F / 0xFF are NaN).  Each tensor carries one float32
+ *       scale: the value of code c is e4m3(c) * x_scale.
+ *   o   : [B,Hq,N,d] bf16 output;  lse : [B,Hq,N] float32 output (natural log
+ *         of the row sum of exp(scale * s_ij), s_ij the scaled-input scores).
+ * Query heads share K/V heads as in fa_fwd_gqa.  Both products run on the
+ * FP8 matrix cores with float32 accumulation.  The probabilities of each key
+ * block are rounded to E4M3 before they multiply V (relative error up to
+ * 2^-4 each, one extra subnormal step below 2^-6 of the running row maximum),
+ * and the row sum is taken over the same rounded values, so o is a convex
+ * combination of rows of V with weights within that rounding of the exact
+ * ones.  q_scale, k_scale, v_scale must be finite and > 0, and
+ * q_scale * k_scale * scale must stay a normal float (FA_ERR_BAD_SCALE).
+ * d in {64, 128}.  Everything else is as for fa_fwd_gqa.
+ */
+FA_API int fa_fwd_fp8(const void *q, const void *k, const void *v,
+               float q_scale, float k_scale, float v_scale, void *o, float *lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               void *stream);
+
 /* A static, human-readable string for a status code (never NULL). */
 FA_API const char *fa_status_string(int status);
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_symbols()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_gqa", "fa_bwd_gqa",
                           "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size",
-                          "fa_status_string", "fa_version"}
+                          "fa_fwd_fp8", "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(lib, n), n
     raw = ctypes.CDLL(fa.LIB_PATH)
@@ -161,6 +161,26 @@ def test_decode_workspace_size():
     assert fa.fa_decode_workspace_size(16, 32, 8, 1, 8192, 128, 0) == 0
     assert fa.fa_decode_workspace_size(16, 32, 7, 1, 8192, 128, 1) == 0
     assert fa.fa_decode_workspace_size(1, 1, 1, 1, 1, 64, 1) >= 64 * 4 + 4
+
+
+def fp8(**kw):
+    a = dict(q=P, k=P, v=P, qs=0.01, ks=0.02, vs=0.5, o=P, lse=P, B=2, Hq=8, Hkv=2, N=1000, d=128, causal=1,
+             scale=0.125, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"], a["B"], a["Hq"],
+                         a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
+    (dict(B=0), 2), (dict(N=0), 2), (dict(Hkv=3), 2), (dict(Hkv=0), 2),
+    (dict(d=256), 3), (dict(d=96), 3),
+    (dict(scale=0.0), 5), (dict(qs=0.0), 5), (dict(ks=-1.0), 5), (dict(vs=float("inf")), 5),
+    (dict(qs=float("nan")), 5), (dict(qs=1e-20, ks=1e-20), 5), (dict(qs=1e30, ks=1e30), 5),
+    (dict(q=P + 8), 6), (dict(k=P + 1), 6), (dict(lse=P + 4), 6), (dict(causal=-1), 8),
+])
+def test_fwd_fp8_validation(kw, code):
+    assert fp8(**kw) == code
 
 
 def test_workspace_size():
