@@ -7,6 +7,8 @@ fewer K/V heads), e.g. gqa_causal_b2hq32hkv4n2048d128; they are timed the same
 way through fa_fwd_gqa / fa_bwd_gqa.  The decode cases (new query rows against
 a key/value cache, e.g. decode_b16hq32hkv8nk8192d128) time one fa_decode call
 per step and report the K/V streaming rate in GB/s against the 8 TB/s HBM peak.
+The FP8 cases (E4M3 inputs with per-tensor scales, e.g. fp8_fwd_b4h16n4096d128)
+time one fa_fwd_fp8 call per step against the dense FP8 matrix-core peak.
 
 A step runs the whole path once over one batch of synthetic inputs that are
 already resident in device memory: fa_fwd (O, lse) then fa_bwd (dQ, dK, dV,
@@ -40,12 +42,15 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd/bwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 5033.2      # dense E4M3, twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "fwd_encoder_b4h16n4096d128"
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_bwd_encoder_b4h16n4096d128_hbm_traffic.md")
 BWD_SOURCES = ["exact_io_aware_49_amd/csrc/fa_bwd_bf16.hip", "exact_io_aware_49_amd/csrc/fa_device.h"]
+FP8_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_fwd_fp8_b4h16n4096d128_hbm_traffic.md")
+FP8_SOURCES = ["exact_io_aware_49_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_49_amd/csrc/fa_device.h"]
 
 
 def sources_sha(paths):
@@ -56,16 +61,16 @@ def sources_sha(paths):
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per backward launch from the committed rocprofv3 counter summary,
-    or None if it is missing or the backward kernels changed since it was taken."""
+def measured_traffic(profile=TRAFFIC_PROFILE, sources=BWD_SOURCES):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None if it
+    is missing or the kernel sources changed since it was taken."""
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(profile).read()
     except OSError:
         return None
     sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     tot = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
-    if not sha or not tot or sha.group(1) != sources_sha(BWD_SOURCES):
+    if not sha or not tot or sha.group(1) != sources_sha(sources):
         return None
     return int(tot.group(1))
 
@@ -75,15 +80,20 @@ def fwd_flops(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
+def _oracle_threads():
+    """Threads numpy's BLAS runs the oracle's matrix products with."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the float64 oracle (forward + backward) on whole query heads until ~budget_s elapse."""
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _oracle_threads()
     B, H, N, d = w.shape
     q, k, v, do = w.inputs()
     g = H // k.shape[1]
@@ -136,6 +146,99 @@ class _Case:
         return inputs.gen_gqa(self.B, self.H, self.hkv, self.N, self.d, "bf16", self.seed, with_do=True)
 
 
+def _time_steps(step, a, stream):
+    """a.warmup untimed calls, then a.steps timed ones: (wall ms per step, mean ms between
+    HIP events recorded on `stream` around each call)."""
+    import torch
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / a.steps, float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+
+def fp8_main(a, name):
+    """One fa_fwd_fp8 call per step; value = forward matrix-product flops / time."""
+    import torch
+
+    import exact_io_aware_49_amd as fa
+    from exact_io_aware_49_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    fa.load_library()
+    c = inputs.FP8_CASES[name]
+    B, hq, hkv, N, d, causal = c["B"], c["hq"], c["hkv"], c["N"], c["d"], bool(c["causal"])
+    (q8, k8, v8), sc = inputs.fp8_case_inputs(c)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q8, k8, v8))
+    o = torch.empty((B, hq, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, hq, N), dtype=torch.float32, device=dev)
+    scale = d ** -0.5
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        rc = fa.fa_fwd_fp8(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), sc[0], sc[1], sc[2], o.data_ptr(),
+                           lse.data_ptr(), B, hq, hkv, N, d, int(causal), scale, stream.cuda_stream)
+        if rc:
+            raise RuntimeError(fa.fa_status_string(rc))
+
+    ms_per_step, launch_ms = _time_steps(step, a, stream)
+    ff = fwd_flops(B, hq, N, d, causal)
+    value = ff / (ms_per_step * 1e-3) / 1e12
+    achieved = ff / (launch_ms * 1e-3) / 1e12
+    line = {
+        "metric": "attention FP8 forward TFLOP/s on 1 MI355X + % of fp8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic: i.i.d. N(0,1) from PCG64, per-tensor scaled to E4M3 codes, resident in HBM",
+        "config": {"workload": name, "pass": "forward", "B": B, "Hq": hq, "Hkv": hkv, "N": N, "d": d,
+                   "causal": causal, "scale": scale},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic(FP8_TRAFFIC_PROFILE, FP8_SOURCES)
+                     if name == "fp8_fwd_b4h16n4096d128" else None,
+                     "kernel": "fa_fwd_fp8_kernel",
+                     "avg_launch_ms": round(launch_ms, 4)},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        import oracle
+        s = float(np.float32(scale))
+        g = hq // hkv
+        heads = 0
+        t0 = time.perf_counter()
+        for b in range(B):
+            for h in range(hq):
+                sq = (slice(b, b + 1), slice(h, h + 1))
+                sk = (slice(b, b + 1), slice(h // g, h // g + 1))
+                oracle.attention_forward_fp8(q8[sq], k8[sk], v8[sk], sc[0], sc[1], sc[2], causal, s)
+                heads += 1
+                if time.perf_counter() - t0 >= a.cpu_budget:
+                    break
+            if time.perf_counter() - t0 >= a.cpu_budget:
+                break
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(fwd_flops(1, heads, N, d, causal) / dt / 1e12, 4),
+                                "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
+                                "sample": f"{heads} of {B * hq} query heads, float64 numpy forward of the "
+                                          f"decoded inputs, {dt:.1f} s wall"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def decode_main(a, name):
     """One fa_decode call per step; value = K/V bytes of the valid cache rows / time."""
     import torch
@@ -168,19 +271,7 @@ def decode_main(a, name):
         if rc:
             raise RuntimeError(fa.fa_status_string(rc))
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    ms_per_step = wall * 1e3 / a.steps
+    ms_per_step, launch_ms = _time_steps(step, a, stream)
     kv_bytes = 2.0 * hkv * float(lens.astype(np.int64).sum()) * d * 2
     io_bytes = kv_bytes + 2.0 * B * hq * nq * d * 2 + B * hq * nq * 4  # + Q read, O and lse written
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -214,7 +305,7 @@ def decode_main(a, name):
                 break
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(2.0 * hkv * rows * d * 2 / dt / 1e9, 3), "unit": "GB/s",
-                                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                "cores": _oracle_threads(), "kind": "oracle",
                                 "sample": f"{done} of {B} sequences, float64 numpy, {dt:.1f} s wall"}
     print(json.dumps(line), flush=True)
     return 0
@@ -240,6 +331,8 @@ def main(argv=None):
     from exact_io_aware_49_amd import inputs as _inputs
     if a.workload in _inputs.DECODE_CASES:
         return decode_main(a, a.workload)
+    if a.workload in _inputs.FP8_CASES:
+        return fp8_main(a, a.workload)
 
     import torch
 

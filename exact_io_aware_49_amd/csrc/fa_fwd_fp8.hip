@@ -22,6 +22,8 @@
 //     for byte t of lane half h), so P packs straight from the accumulators
 //     and V^T is read from the row-major tile with ds_read_b64_tr_b8 (a lane
 //     gets one column of 8 consecutive rows).
+//   * LDS operand reads are ordinary loads (and the tr8 builtin), so the
+//     compiler counts them and may move them ahead of their use.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -29,6 +31,7 @@ namespace fa {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ floatx16 mfma_fp8(const i32x8 &a, const i32x8 &b, const floatx16 &c) {
   // E4M3 x E4M3 (format codes 0, 0), block scale exponents 127 (2^0)
@@ -41,13 +44,13 @@ __device__ __forceinline__ int pack_fp8x2(float a, float b, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
-// ds_read_b64_tr_b8 at addr + OFF (inline asm: waited for with lds_wait)
-template <int OFF>
-__device__ __forceinline__ u32x2 ds_read_tr8_at(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
-  return r;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+// LDS reads the compiler can schedule and count (lgkmcnt) itself
+__device__ __forceinline__ i32x2 lds_tr8(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2 *)(uintptr_t)addr);
+}
+__device__ __forceinline__ i32x4 lds_b128(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) i32x4 *)(uintptr_t)addr;
 }
 
 // LDS swizzles (16-byte chunk index ^ f(row)).  A 256-byte bank cycle holds
@@ -169,6 +172,7 @@ fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, 
   floatx16 oacc[C::CT];
 #pragma unroll
   for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = floatx16{0};
+  int pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // packed P, every byte rewritten per tile
   floatx16 lsum = floatx16{0};  // every register: this lane's row sum of the rounded P
   float m_ref = -INFINITY;      // reference maximum of the raw (unscaled) scores
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
@@ -183,10 +187,9 @@ fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, 
       constexpr int KT = decltype(ktc)::value;
 #pragma unroll
       for (int ks = 0; ks < C::KS8; ++ks) {
-        u32x4 lo = ds_read_b128_at<KOFF + 32 * KT * RB>(kaddr[ks][0]);
-        u32x4 hi = ds_read_b128_at<KOFF + 32 * KT * RB>(kaddr[ks][1]);
-        lds_wait(lo, hi);
-        const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const i32x4 lo = lds_b128(kaddr[ks][0] + KOFF + 32 * KT * RB);
+        const i32x4 hi = lds_b128(kaddr[ks][1] + KOFF + 32 * KT * RB);
+        const i32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         s[KT] = mfma_fp8(a, qf[ks], s[KT]);
       }
     });
@@ -236,7 +239,6 @@ fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, 
     // ---- scores of tile t+1 (independent of the softmax below; the last tile's are discarded)
     scores(std::integral_constant<int, (BUF ^ 1) * TB>{}, nxt);
     // ---- P of tile t as E4M3, byte 16 kt + r = key 32 kt + 16 (r / 8) + 8 half + r % 8
-    int pw[8];
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
@@ -245,19 +247,18 @@ fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, 
         const float p1 = fast_exp2(__builtin_fmaf(cur[kt][4 * w + 1], score_log2e, -mc));
         const float p2 = fast_exp2(__builtin_fmaf(cur[kt][4 * w + 2], score_log2e, -mc));
         const float p3 = fast_exp2(__builtin_fmaf(cur[kt][4 * w + 3], score_log2e, -mc));
-        pw[4 * kt + w] = pack_fp8x2<true>(p2, p3, pack_fp8x2<false>(p0, p1, 0));
+        pw[4 * kt + w] = pack_fp8x2<true>(p2, p3, pack_fp8x2<false>(p0, p1, pw[4 * kt + w]));
       }
     const i32x8 pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     // ---- O^T += V^T P^T (one 64-key step per column tile) and the row sum
 #pragma unroll
     for (int ct = 0; ct < C::CT; ++ct) {
       constexpr int VOFF = BUF * TB;
-      u32x2 g0 = ds_read_tr8_at<VOFF>(vaddr[ct]);
-      u32x2 g1 = ds_read_tr8_at<VOFF + 16 * RB>(vaddr[ct]);
-      u32x2 g2 = ds_read_tr8_at<VOFF + 32 * RB>(vaddr[ct]);
-      u32x2 g3 = ds_read_tr8_at<VOFF + 48 * RB>(vaddr[ct]);
-      lds_wait(g0, g1, g2, g3);
-      const i32x8 a = {(int)g0[0], (int)g0[1], (int)g1[0], (int)g1[1], (int)g2[0], (int)g2[1], (int)g3[0], (int)g3[1]};
+      const i32x2 g0 = lds_tr8(vaddr[ct] + VOFF);
+      const i32x2 g1 = lds_tr8(vaddr[ct] + VOFF + 16 * RB);
+      const i32x2 g2 = lds_tr8(vaddr[ct] + VOFF + 32 * RB);
+      const i32x2 g3 = lds_tr8(vaddr[ct] + VOFF + 48 * RB);
+      const i32x8 a = {g0[0], g0[1], g1[0], g1[1], g2[0], g2[1], g3[0], g3[1]};
       oacc[ct] = mfma_fp8(a, pb, oacc[ct]);
     }
     lsum = mfma_fp8(ones, pb, lsum);
