@@ -18,12 +18,12 @@ constexpr int kVersion = 10000;  // 1.0.0
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_common(int B, int H, int N, int d, int causal, float scale, int dtype, bool fwd) {
+int check_common(int B, int H, int N, int d, int causal, float scale, int dtype) {
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED_HEAD_DIM;
-  // head dim 256: bf16 forward only
-  if (d == 256 && (dtype != FA_DTYPE_BF16 || !fwd)) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+  // head dim 256: bf16 only
+  if (d == 256 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_HEAD_DIM;
   // B*H*N rows must stay below 2^55 (so B*H*N*d < 2^62), and the launch grids
   // (at most one workgroup per 64 rows of each head) must fit in 2^31 - 1.
   const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
@@ -73,7 +73,7 @@ const char *fa_status_string(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a required pointer is NULL";
     case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H and N must be >= 1, the tensor size must fit, and the query heads must split evenly over the K/V heads";
-    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM: head dim d must be 64 or 128 (256: bf16 forward only)";
+    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM: head dim d must be 64 or 128 (256: bf16 forward and backward only)";
     case FA_ERR_UNSUPPORTED_DTYPE: return "FA_ERR_UNSUPPORTED_DTYPE: dtype not supported by this entry point";
     case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite and > 0";
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
@@ -87,7 +87,7 @@ const char *fa_status_string(int status) {
 int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int N,
                int d, int causal, float scale, int dtype, void *stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
-  int st = check_common(B, Hq, N, d, causal, scale, dtype, true);
+  int st = check_common(B, Hq, N, d, causal, scale, dtype);
   if (st == FA_OK) st = check_heads(Hq, Hkv);
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -109,7 +109,7 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
 int fa_fwd_fp8(const void *q, const void *k, const void *v, float q_scale, float k_scale, float v_scale, void *o,
                float *lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale, void *stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
-  int st = check_common(B, Hq, N, d, causal, scale, FA_DTYPE_BF16, true);
+  int st = check_common(B, Hq, N, d, causal, scale, FA_DTYPE_BF16);
   if (st == FA_OK) st = check_heads(Hq, Hkv);
   if (st != FA_OK) return st;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
@@ -125,7 +125,7 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, float q_scale, float
 }
 
 size_t fa_bwd_gqa_workspace_size(int B, int Hq, int Hkv, int N, int d, int dtype) {
-  if (check_common(B, Hq, N, d, 0, 1.0f, dtype, false) != FA_OK || check_heads(Hq, Hkv) != FA_OK ||
+  if (check_common(B, Hq, N, d, 0, 1.0f, dtype) != FA_OK || check_heads(Hq, Hkv) != FA_OK ||
       dtype != FA_DTYPE_BF16)
     return 0;
   // D_i and lse_i * log2(e), one float32 each per query row; with the query
@@ -147,7 +147,7 @@ int fa_bwd_gqa(const void *q, const void *k, const void *v, const void *o, const
                void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                int N, int d, int causal, float scale, int dtype, void *stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
-  int st = check_common(B, Hq, N, d, causal, scale, dtype, false);
+  int st = check_common(B, Hq, N, d, causal, scale, dtype);
   if (st == FA_OK) st = check_heads(Hq, Hkv);
   if (st != FA_OK) return st;
   if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;

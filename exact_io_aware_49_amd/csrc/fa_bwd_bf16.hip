@@ -103,10 +103,13 @@ __device__ __forceinline__ void mfma_transposed(floatx16 (&acc)[D / 32], const T
                                                 const bf16x8 &b) {
 #pragma unroll
   for (int c2 = 0; c2 < D / 32; c2 += 2) {
-    u32x2 l0 = ds_read_tr16_at<OFF>(to.trans[c2][0]);
-    u32x2 h0 = ds_read_tr16_at<OFF>(to.trans[c2][1]);
-    u32x2 l1 = ds_read_tr16_at<OFF>(to.trans[c2 + 1][0]);
-    u32x2 h1 = ds_read_tr16_at<OFF>(to.trans[c2 + 1][1]);
+    // the instruction's offset field holds 16 bits; larger displacements go into the address
+    constexpr int HI = OFF & ~0xffff;
+    constexpr int LO = OFF & 0xffff;
+    u32x2 l0 = ds_read_tr16_at<LO>(to.trans[c2][0] + HI);
+    u32x2 h0 = ds_read_tr16_at<LO>(to.trans[c2][1] + HI);
+    u32x2 l1 = ds_read_tr16_at<LO>(to.trans[c2 + 1][0] + HI);
+    u32x2 h1 = ds_read_tr16_at<LO>(to.trans[c2 + 1][1] + HI);
     lds_wait(l0, h0, l1, h1);
     const u32x4 a0 = {l0[0], l0[1], h0[0], h0[1]};
     const u32x4 a1 = {l1[0], l1[1], h1[0], h1[1]};
@@ -148,7 +151,7 @@ __device__ __forceinline__ void store_rows_bf16(__bf16 *row, const floatx16 (&ac
 
 // ============================================================== dQ kernel
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, (D == 256) ? 1 : 2)
 fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                  const __bf16 *__restrict__ Og, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
                  __bf16 *__restrict__ dQ, float *__restrict__ Dsum, float *__restrict__ Lse2, int N,
@@ -279,8 +282,10 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
 }
 
 // ============================================================== dK/dV kernel
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 3)
+// WHAT: 3 = dK and dV, 1 = dV only, 2 = dK only (head dim 256 runs the two
+// halves as separate launches: one wave cannot hold both accumulators there)
+template <int D, bool CAUSAL, int WHAT = 3>
+__global__ void __launch_bounds__(256, (D == 256) ? 1 : 3)
 fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                    const __bf16 *__restrict__ dO, const float *__restrict__ Dsum, const float *__restrict__ Lse2,
                    __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, float *__restrict__ part, int N, int group,
@@ -314,6 +319,8 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
   const int my_k = kw0 + l32;
   const bool k_ok = my_k < N;
 
+  constexpr bool DO_K = (WHAT & 2) != 0;
+  constexpr bool DO_V = (WHAT & 1) != 0;
   bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
   {
     const size_t roff = head_off + (size_t)(k_ok ? my_k : 0) * D + 8 * half;
@@ -321,7 +328,7 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       const u32x4 z = {0, 0, 0, 0};
       kf[ks] = as_bf16x8(k_ok ? ld16(K + roff + 16 * ks) : z);
-      vf[ks] = as_bf16x8(k_ok ? ld16(V + roff + 16 * ks) : z);
+      if constexpr (DO_K) vf[ks] = as_bf16x8(k_ok ? ld16(V + roff + 16 * ks) : z);
     }
   }
 
@@ -365,17 +372,20 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
     static_for<2>([&](auto qtc) {
       constexpr int QT = decltype(qtc)::value;
       floatx16 s = floatx16{0}, dp = floatx16{0};
-      {
-        bf16x8 a[C::KSTEPS], b[C::KSTEPS];
+      // operand rows in groups of RCH k-steps (all at once below d = 256)
+      constexpr int RCH = (D == 256) ? 4 : C::KSTEPS;
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) {
-          a[ks] = as_bf16x8(ld16(Qs + to.rows[ks] + 32 * QT * RB));
-          b[ks] = as_bf16x8(ld16(Os + to.rows[ks] + 32 * QT * RB));
+      for (int k0 = 0; k0 < C::KSTEPS; k0 += RCH) {
+        bf16x8 a[RCH], b[RCH];
+#pragma unroll
+        for (int i = 0; i < RCH; ++i) {
+          a[i] = as_bf16x8(ld16(Qs + to.rows[k0 + i] + 32 * QT * RB));
+          if constexpr (DO_K) b[i] = as_bf16x8(ld16(Os + to.rows[k0 + i] + 32 * QT * RB));
         }
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) {
-          s = mfma32x32x16(a[ks], kf[ks], s);
-          dp = mfma32x32x16(b[ks], vf[ks], dp);
+        for (int i = 0; i < RCH; ++i) {
+          s = mfma32x32x16(a[i], kf[k0 + i], s);
+          if constexpr (DO_K) dp = mfma32x32x16(b[i], vf[k0 + i], dp);
         }
       }
       static_for<2>([&](auto mc) {
@@ -383,8 +393,11 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
         const int qoff = 32 * QT + 16 * M + 8 * half;  // tile-local query of register 8M
         const floatx4 l0 = *reinterpret_cast<const floatx4 *>(lst + qoff);
         const floatx4 l1 = *reinterpret_cast<const floatx4 *>(lst + qoff + 4);
-        const floatx4 d0 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff);
-        const floatx4 d1 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff + 4);
+        floatx4 d0 = floatx4{0}, d1 = floatx4{0};
+        if constexpr (DO_K) {
+          d0 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff);
+          d1 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff + 4);
+        }
         u32x4 pw, sw;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -406,8 +419,8 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
           sw[i] = pack_bf16x2(s2[0], s2[1]);
         }
         constexpr int OFFQ = BUF * STAGE + 16 * (2 * QT + M) * RB;
-        mfma_transposed<D, OFFQ + TB>(dvacc, to, as_bf16x8(pw));  // dV^T += dO^T P
-        mfma_transposed<D, OFFQ>(dkacc, to, as_bf16x8(sw));       // dK^T += Q^T dS
+        if constexpr (DO_V) mfma_transposed<D, OFFQ + TB>(dvacc, to, as_bf16x8(pw));  // dV^T += dO^T P
+        if constexpr (DO_K) mfma_transposed<D, OFFQ>(dkacc, to, as_bf16x8(sw));       // dK^T += Q^T dS
       });
     });
   };
@@ -428,13 +441,13 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
 
   if (k_ok) {
     if (nsplit == 1) {
-      store_rows_bf16<D>(dK + head_off + (size_t)my_k * D, dkacc, scale, half);
-      store_rows_bf16<D>(dV + head_off + (size_t)my_k * D, dvacc, 1.0f, half);
+      if constexpr (DO_K) store_rows_bf16<D>(dK + head_off + (size_t)my_k * D, dkacc, scale, half);
+      if constexpr (DO_V) store_rows_bf16<D>(dV + head_off + (size_t)my_k * D, dvacc, 1.0f, half);
     } else {  // partials [2][nsplit][K/V heads][N][D]: dK (scaled) then dV
       const size_t per = (size_t)nkvh * N * D;
       const size_t off = (size_t)split * per + head_off + (size_t)my_k * D;
-      store_rows_f32<D>(part + off, dkacc, scale, half);
-      store_rows_f32<D>(part + (size_t)nsplit * per + off, dvacc, 1.0f, half);
+      if constexpr (DO_K) store_rows_f32<D>(part + off, dkacc, scale, half);
+      if constexpr (DO_V) store_rows_f32<D>(part + (size_t)nsplit * per + off, dvacc, 1.0f, half);
     }
   }
 }
@@ -689,6 +702,18 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
                        (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
                        nsplit, c, scale);
+  else if constexpr (D == 256) {
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, 1>), dim3((unsigned)gk), dim3(256), 0, stream,
+                       (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
+                       (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
+                       nsplit, c, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, 2>), dim3((unsigned)gk), dim3(256), 0, stream,
+                       (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
+                       (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
+                       nsplit, c, scale);
+  }
   else
     hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(512), 0, stream,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
@@ -712,8 +737,11 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   if (d == 64)
     return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream)
                   : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream);
-  return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream)
-                : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream);
+  if (d == 128)
+    return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream)
+                  : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream);
+  return causal ? launch<256, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream)
+                : launch<256, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream);
 }
 
 }  // namespace fa

@@ -198,14 +198,16 @@ __device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t rsrc, void *lds
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Chunk permutation for a row-major bf16 tile of d = 64 or 128 columns that is
+// Chunk permutation for a row-major bf16 tile of d = 64, 128 or 256 columns that is
 // read both as rows (16 consecutive rows, one 16-byte chunk each: the A operand
 // of a 32x32x16 MFMA) and transposed (ds_read_b64_tr_b16: 4 consecutive rows x
 // 4 chunks per 32 lanes).  physical chunk = logical chunk ^ swz_rt(row); both
-// patterns then hit 64 distinct banks.  Rows 16 apart share a permutation.
+// patterns then hit 64 distinct banks.  Rows 16 apart share a permutation.  At
+// d >= 128 a row is a whole number of 256-byte bank cycles, so d = 256 uses the
+// d = 128 pattern on its first 16 chunks (chunks 16..31 keep bit 4).
 template <int D>
 __device__ __forceinline__ int swz_rt(int r) {
-  return (D == 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  return (D >= 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // Chunk permutations of a streamed K or V tile (physical chunk = logical

@@ -31,8 +31,9 @@
  *    (positions counted from 0; queries and keys have the same length N).
  *    Masked scores get probability exactly 0.
  *  - scale must be finite and > 0 (the pages' value is 1/sqrt(d)).
- *  - Supported: d in {64, 128}, and d = 256 for the bf16 forward (fa_fwd /
- *    fa_fwd_gqa; other calls with d = 256 return FA_ERR_UNSUPPORTED_HEAD_DIM);
+ *  - Supported: d in {64, 128}, and d = 256 in bf16 (fa_fwd, fa_bwd and their
+ *    _gqa forms; the fp32 forward, fa_decode and fa_fwd_fp8 return
+ *    FA_ERR_UNSUPPORTED_HEAD_DIM for it);
  *    B, H, N >= 1; B*H*N*d < 2^62; one head's N*d elements below 2^31 bytes
  *    (N < 8,388,608 for bf16 at d = 128).
  */
@@ -60,7 +61,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL_POINTER = 1,         /* a required pointer is NULL */
   FA_ERR_BAD_SHAPE = 2,            /* B, H or N < 1, the element count overflows, or Hq % Hkv != 0 */
-  FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128} (256: bf16 forward only) */
+  FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128} (256: bf16 forward and backward only) */
   FA_ERR_UNSUPPORTED_DTYPE = 4,    /* dtype unknown, or not supported by this entry point */
   FA_ERR_BAD_SCALE = 5,            /* scale not finite or not > 0 */
   FA_ERR_MISALIGNED = 6,           /* a tensor pointer is not 16-byte aligned */
@@ -108,8 +109,9 @@ FA_API size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
  * Only FA_DTYPE_BF16 is supported (FA_ERR_UNSUPPORTED_DTYPE otherwise).
  * Two kernels run on `stream`: one owns a block of queries and produces dq
  * (and the per-row D and scaled lse in the workspace), the other owns a block
- * of keys and produces dk and dv.  No atomics are used, so dq, dk and dv are
- * bitwise reproducible.
+ * of keys and produces dk and dv (at d = 256 two launches of it, one for dv
+ * and one for dk, since one wave cannot hold both accumulators).  No atomics
+ * are used, so dq, dk and dv are bitwise reproducible.
  */
 FA_API int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            const void *dout, const float *lse, void *dq, void *dk, void *dv,

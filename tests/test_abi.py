@@ -75,7 +75,8 @@ def test_fwd_validation(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(do=None), 1), (dict(dq=None), 1), (dict(lse=None), 1),
-    (dict(N=0), 2), (dict(d=80), 3), (dict(d=256), 3), (dict(dtype=0), 4), (dict(scale=0.0), 5),
+    (dict(N=0), 2), (dict(d=80), 3), (dict(d=512), 3), (dict(dtype=0), 4), (dict(d=256, dtype=0), 3),
+    (dict(scale=0.0), 5),
     (dict(ws=None), 7), (dict(wsb=100), 7), (dict(dk=P + 8), 6), (dict(ws=P + 8), 6), (dict(causal=3), 8),
 ])
 def test_bwd_validation(kw, code):
@@ -188,7 +189,8 @@ def test_workspace_size():
     assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 1) == 256
     assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 0) == 0   # fp32 backward unsupported
     assert fa.fa_bwd_workspace_size(1, 1, 3, 96, 1) == 0
-    assert fa.fa_bwd_workspace_size(1, 1, 3, 256, 1) == 0  # head dim 256: forward only
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 256, 1) == 256  # head dim 256: bf16 backward too
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 256, 0) == 0
     assert fa.fa_bwd_workspace_size(0, 1, 3, 64, 1) == 0
 
 

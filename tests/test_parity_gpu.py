@@ -206,6 +206,19 @@ def test_fwd_d256_heads():
     say(f"   O max/rel {eo[0]:.2e}/{eo[1]:.2e}  lse max {el[0]:.2e}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_d256(causal):
+    """Head dim 256, bf16 backward (dQ kernel at one wave per SIMD; dV and dK from two
+    launches of the key-owner kernel): ragged lengths, then B=1 H=4 N=1024 on every head."""
+    need_gpu()
+    for i, N in enumerate([1, 17, 64, 100, 129, 300]):
+        q, k, v, do = inputs.gen_qkv((1 + i % 2, 1 + i % 3, N, 256), "bf16", 1400 + 7 * i, with_do=True)
+        heads = [(b, h) for b in range(q.shape[0]) for h in range(q.shape[1])]
+        check_bwd_heads(q, k, v, do, causal, 256 ** -0.5, heads, f"d256 sweep N={N}")
+    q, k, v, do = inputs.gen_qkv((1, 4, 1024, 256), "bf16", 1450 + causal, with_do=True)
+    check_bwd_heads(q, k, v, do, causal, 256 ** -0.5, [(0, h) for h in range(4)], "d256 B1 H4 N1024")
+
+
 # ------------------------------------------------------------------ shared K/V heads
 
 def _gqa_check(case_name, heads_b0):
@@ -262,7 +275,7 @@ def test_mqa_d64():
     _gqa_check("mqa_b2hq16hkv1n1024d64", [0])
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa_sweep(d, causal):
     """Ragged lengths and group sizes 1..4 against the oracle on every head (dK and dV
