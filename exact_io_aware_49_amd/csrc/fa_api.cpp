@@ -21,9 +21,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_common(int B, int H, int N, int d, int causal, float scale, int dtype) {
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED_HEAD_DIM;
-  // head dim 256: bf16 only
-  if (d == 256 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+  // head dims 32, 96 and 256: bf16 only
+  if ((d == 32 || d == 96 || d == 256) && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_HEAD_DIM;
   // B*H*N rows must stay below 2^55 (so B*H*N*d < 2^62), and the launch grids
   // (at most one workgroup per 64 rows of each head) must fit in 2^31 - 1.
   const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
@@ -73,7 +73,7 @@ const char *fa_status_string(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a required pointer is NULL";
     case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H and N must be >= 1, the tensor size must fit, and the query heads must split evenly over the K/V heads";
-    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM: head dim d must be 64 or 128 (256: bf16 forward and backward only)";
+    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM: head dim d must be 64 or 128 (32, 96, 256: bf16 forward and backward only)";
     case FA_ERR_UNSUPPORTED_DTYPE: return "FA_ERR_UNSUPPORTED_DTYPE: dtype not supported by this entry point";
     case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite and > 0";
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";

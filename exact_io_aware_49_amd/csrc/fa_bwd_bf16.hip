@@ -44,8 +44,12 @@ struct BwdCfg {
   static constexpr int TROWS = 64;            // rows of a streamed tile
   static constexpr int KSTEPS = D / 16;
   static constexpr int CT = D / 32;
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int RB = 2 * D;            // bytes per row
+  // LDS rows are DL columns wide: d = 96 sits in a 128-column layout whose last
+  // four 16-byte chunks read as zero
+  static constexpr int DL = (D == 96) ? 128 : D;
+  static constexpr int CPR = DL / 8;          // 16-byte chunks per LDS row
+  static constexpr int RB = 2 * DL;           // bytes per LDS row
+  static constexpr int RBG = 2 * D;           // bytes per row in global memory
   static constexpr int RPI = 1024 / RB;       // rows per wave-wide 16-byte load
   static constexpr int TB = TROWS * RB;       // bytes per tile
   static constexpr int LPW = TB / 1024 / 4;   // loads per wave per tile
@@ -62,7 +66,10 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rs, unsigned c
   for (int u = 0; u < LPW; ++u) {
     const int row0 = (wave * LPW + u) * C::RPI;
     const int row = row0 + lane / C::CPR;
-    const uint32_t g = (uint32_t)(r0 + row) * C::RB + 16u * ((lane % C::CPR) ^ swz_rt<D>(row));
+    const int c = (lane % C::CPR) ^ swz_rt<C::DL>(row);
+    uint32_t g = (uint32_t)(r0 + row) * C::RBG + 16u * c;
+    if constexpr (C::DL != D)
+      if (c >= D / 8) g = 0x80000000u;  // padding chunk: past the buffer, reads zero
     load_lds16(rs, dst + row0 * C::RB, g);
   }
 }
@@ -81,7 +88,7 @@ struct TileOffsets {
     const int half = lane >> 5;
     const int r = swap_bits23(lane & 31);
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) rows[ks] = r * C::RB + 16 * ((2 * ks + half) ^ swz_rt<D>(r));
+    for (int ks = 0; ks < C::KSTEPS; ++ks) rows[ks] = r * C::RB + 16 * ((2 * ks + half) ^ swz_rt<C::DL>(r));
     const int rlo = 8 * half + ((lane & 15) >> 2);
     const int tq = lane & 3;
 #pragma unroll
@@ -90,7 +97,7 @@ struct TileOffsets {
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {
         const int rr = rlo + 4 * hi;
-        trans[ct][hi] = trans_base + rr * C::RB + 16 * (ch ^ swz_rt<D>(rr)) + 8 * (tq & 1);
+        trans[ct][hi] = trans_base + rr * C::RB + 16 * (ch ^ swz_rt<C::DL>(rr)) + 8 * (tq & 1);
       }
     }
   }
@@ -101,8 +108,18 @@ struct TileOffsets {
 template <int D, int OFF>
 __device__ __forceinline__ void mfma_transposed(floatx16 (&acc)[D / 32], const TileOffsets<D> &to,
                                                 const bf16x8 &b) {
+  if constexpr (D / 32 % 2 == 1) {  // an odd column group count: the last one alone
+    constexpr int c = D / 32 - 1;
+    constexpr int HI = OFF & ~0xffff;
+    constexpr int LO = OFF & 0xffff;
+    u32x2 l0 = ds_read_tr16_at<LO>(to.trans[c][0] + HI);
+    u32x2 h0 = ds_read_tr16_at<LO>(to.trans[c][1] + HI);
+    lds_wait(l0, h0);
+    const u32x4 a0 = {l0[0], l0[1], h0[0], h0[1]};
+    acc[c] = mfma32x32x16(as_bf16x8(a0), b, acc[c]);
+  }
 #pragma unroll
-  for (int c2 = 0; c2 < D / 32; c2 += 2) {
+  for (int c2 = 0; c2 + 1 < D / 32; c2 += 2) {
     // the instruction's offset field holds 16 bits; larger displacements go into the address
     constexpr int HI = OFF & ~0xffff;
     constexpr int LO = OFF & 0xffff;
@@ -208,7 +225,7 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
   int ntiles = (N + 63) / 64;
   if (CAUSAL) ntiles = min(ntiles, (min(q0 + BR, N) - 1) / 64 + 1);
 
-  const uint32_t head_bytes = (uint32_t)N * RB;
+  const uint32_t head_bytes = (uint32_t)N * C::RBG;
   const size_t kv_off = (size_t)(bh / group) * N * D;  // the K/V head this query head reads
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, head_bytes);
@@ -285,7 +302,7 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
 // WHAT: 3 = dK and dV, 1 = dV only, 2 = dK only (head dim 256 runs the two
 // halves as separate launches: one wave cannot hold both accumulators there)
 template <int D, bool CAUSAL, int WHAT = 3>
-__global__ void __launch_bounds__(256, (D == 256) ? 1 : 3)
+__global__ void __launch_bounds__(256, (D == 256) ? 1 : (D == 96) ? 2 : 3)
 fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                    const __bf16 *__restrict__ dO, const float *__restrict__ Dsum, const float *__restrict__ Lse2,
                    __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, float *__restrict__ part, int N, int group,
@@ -335,7 +352,7 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
   const int nqt = (N + 63) / 64;
   const int qt0 = CAUSAL ? (kb0 / 64) : 0;
 
-  const uint32_t head_bytes = (uint32_t)N * RB;
+  const uint32_t head_bytes = (uint32_t)N * C::RBG;
   // query heads g0 .. g1-1 of the group are this workgroup's share
   const int g0 = (int)((long long)split * group / nsplit);
   const int g1 = (int)((long long)(split + 1) * group / nsplit);
@@ -504,7 +521,7 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
   const int nqt = (N + 63) / 64;
   const int qt0 = CAUSAL ? (kb0 / 64) : 0;
 
-  const uint32_t head_bytes = (uint32_t)N * RB;
+  const uint32_t head_bytes = (uint32_t)N * C::RBG;
   // query heads g0 .. g1-1 of the group are this workgroup's share
   const int g0 = (int)((long long)split * group / nsplit);
   const int g1 = (int)((long long)(split + 1) * group / nsplit);
@@ -697,7 +714,7 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
                      (const __bf16 *)dout, lse, (__bf16 *)dq, dsum, lse2, N, group, c, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (D == 64)
+  if constexpr (D != 128 && D != 256)
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, stream,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
                        (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
@@ -734,6 +751,12 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const void *dout,
                            const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int H, int group,
                            int N, int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 96)
+    return causal ? launch<96, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream)
+                  : launch<96, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream);
+  if (d == 32)
+    return causal ? launch<32, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream)
+                  : launch<32, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream);
   if (d == 64)
     return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream)
                   : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, group, N, scale, stream);

@@ -207,6 +207,7 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // d = 128 pattern on its first 16 chunks (chunks 16..31 keep bit 4).
 template <int D>
 __device__ __forceinline__ int swz_rt(int r) {
+  if constexpr (D == 32) return (r >> 2) & 3;  // four 64-byte rows per bank cycle
   return (D >= 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
@@ -217,10 +218,12 @@ __device__ __forceinline__ int swz_rt(int r) {
 // is a multiple of the 256-byte bank cycle, so d = 128 and d = 256 share them.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
+  if constexpr (D == 32) return (r >> 2) & 3;
   return (D >= 128) ? (r & 15) : ((r >> 1) & 7);
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
+  if constexpr (D == 32) return (r >> 2) & 3;  // the 4 rows of a transposed read share a value
   return (D >= 128) ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 

@@ -56,8 +56,12 @@ struct FwdCfg {
   static constexpr int NKT = BC / 32;               // 32-key score tiles per K/V tile
   static constexpr int KSTEPS = D / 16;             // MFMA k-steps over the head dim
   static constexpr int CT = D / 32;                 // 32-column output tiles
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int ROW_BYTES = D * 2;
+  // LDS rows are DL columns wide: d = 96 sits in a 128-column layout whose last
+  // four 16-byte chunks read as zero
+  static constexpr int DL = (D == 96) ? 128 : D;
+  static constexpr int CPR = DL / 8;                // 16-byte chunks per LDS row
+  static constexpr int ROW_BYTES = DL * 2;          // bytes per LDS row
+  static constexpr int GROW_BYTES = D * 2;          // bytes per row in global memory
   static constexpr int RPI = 1024 / ROW_BYTES;      // rows per wave-wide 16-byte load
   static constexpr int TILE_BYTES = BC * ROW_BYTES;
   static constexpr int LPW = TILE_BYTES / 1024 / 4; // loads per wave per tensor per tile
@@ -88,7 +92,7 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 
   const size_t head_off = (size_t)bh * (size_t)N * D;          // query head: Q, O
   const size_t kv_off = (size_t)(bh / group) * (size_t)N * D;  // its K/V head (group query heads share one)
-  const uint32_t head_bytes = (uint32_t)N * RB;
+  const uint32_t head_bytes = (uint32_t)N * C::GROW_BYTES;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, head_bytes);
 
@@ -113,13 +117,19 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   // ---- direct loads: wave w fills rows [(w*LPW + u)*RPI, +RPI) of a tile
   const int ld_row_in = lane / C::CPR;
   const int ld_chunk = lane % C::CPR;
+  // global byte offset of 16-byte chunk c of key row `row`; chunks past the row
+  // (padding of a d = 96 layout) get an offset beyond the buffer, which reads zero
+  auto goff = [&](int row, int c) -> uint32_t {
+    if constexpr (C::DL != D)
+      if (c >= D / 8) return 0x80000000u;
+    return (uint32_t)row * C::GROW_BYTES + 16u * c;
+  };
   auto issue_k = [&](int t, int lds_off) {
 #pragma unroll
     for (int u = 0; u < C::LPW; ++u) {
       const int row0 = (wave * C::LPW + u) * C::RPI;
       const int row = row0 + ld_row_in;
-      const uint32_t g = (uint32_t)(t * C::BC + row) * RB + 16u * (ld_chunk ^ swz_k<D>(row));
-      load_lds16(krs, smem + lds_off + row0 * RB, g);
+      load_lds16(krs, smem + lds_off + row0 * RB, goff(t * C::BC + row, ld_chunk ^ swz_k<C::DL>(row)));
     }
   };
   auto issue_v = [&](int t, int lds_off) {
@@ -127,8 +137,7 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     for (int u = 0; u < C::LPW; ++u) {
       const int row0 = (wave * C::LPW + u) * C::RPI;
       const int row = row0 + ld_row_in;
-      const uint32_t g = (uint32_t)(t * C::BC + row) * RB + 16u * (ld_chunk ^ swz_v<D>(row));
-      load_lds16(vrs, smem + lds_off + row0 * RB, g);
+      load_lds16(vrs, smem + lds_off + row0 * RB, goff(t * C::BC + row, ld_chunk ^ swz_v<C::DL>(row)));
     }
   };
 
@@ -139,7 +148,7 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   {
     const int r = swap_bits23(l32);
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) koff[ks] = r * RB + 16 * ((2 * ks + half) ^ swz_k<D>(r));
+    for (int ks = 0; ks < C::KSTEPS; ++ks) koff[ks] = r * RB + 16 * ((2 * ks + half) ^ swz_k<C::DL>(r));
   }
   // value A operand (transposed read): lane j = l & 15 of its 16-lane group
   // addresses row key0 + (j >> 2), columns 32*ct + 16*((l >> 4) & 1) + 4*(j & 3)
@@ -154,7 +163,7 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {
         const int r = rlo + 4 * hi;
-        voff[ct][hi] = vb + r * RB + 16 * (ch ^ swz_v<D>(r)) + 8 * (tq & 1);
+        voff[ct][hi] = vb + r * RB + 16 * (ch ^ swz_v<C::DL>(r)) + 8 * (tq & 1);
       }
     }
   }
@@ -228,7 +237,9 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     const bool act = !CAUSAL || (kb <= qw0 + 31);
 
     Frag fa, fb;
-    constexpr bool AHEAD = D < 256;  // at d = 256 a second fragment set does not fit
+    // fragments one chunk ahead at d = 64 and 128; at d = 256 a second set does not
+    // fit, and at d = 32 a chunk has too little work to hide the reads behind
+    constexpr bool AHEAD = (D == 64 || D == 96 || D == 128);
     if (AHEAD && act) read_frag(bufc, std::integral_constant<int, 0>{}, fa);
     float mc = 0.f;
     if (act) {
@@ -364,6 +375,10 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                            int group, int N, int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 96) return causal ? launch<96, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
+                             : launch<96, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
+  if (d == 32) return causal ? launch<32, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
+                             : launch<32, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
   if (d == 64) return causal ? launch<64, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
                              : launch<64, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
   if (d == 256) return causal ? launch<256, true>(q, k, v, o, lse, B, H, group, N, scale, stream)

@@ -31,9 +31,9 @@
  *    (positions counted from 0; queries and keys have the same length N).
  *    Masked scores get probability exactly 0.
  *  - scale must be finite and > 0 (the pages' value is 1/sqrt(d)).
- *  - Supported: d in {64, 128}, and d = 256 in bf16 (fa_fwd, fa_bwd and their
- *    _gqa forms; the fp32 forward, fa_decode and fa_fwd_fp8 return
- *    FA_ERR_UNSUPPORTED_HEAD_DIM for it);
+ *  - Supported: d in {64, 128}, and d in {32, 96, 256} in bf16 (fa_fwd, fa_bwd
+ *    and their _gqa forms; the fp32 forward, fa_decode and fa_fwd_fp8 return
+ *    FA_ERR_UNSUPPORTED_HEAD_DIM for them);
  *    B, H, N >= 1; B*H*N*d < 2^62; one head's N*d elements below 2^31 bytes
  *    (N < 8,388,608 for bf16 at d = 128).
  */
@@ -61,7 +61,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL_POINTER = 1,         /* a required pointer is NULL */
   FA_ERR_BAD_SHAPE = 2,            /* B, H or N < 1, the element count overflows, or Hq % Hkv != 0 */
-  FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128} (256: bf16 forward and backward only) */
+  FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128} (32, 96, 256: bf16 forward and backward only) */
   FA_ERR_UNSUPPORTED_DTYPE = 4,    /* dtype unknown, or not supported by this entry point */
   FA_ERR_BAD_SCALE = 5,            /* scale not finite or not > 0 */
   FA_ERR_MISALIGNED = 6,           /* a tensor pointer is not 16-byte aligned */

@@ -63,7 +63,8 @@ def bwd(**kw):
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
     (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(B=1 << 30, H=1 << 30), 2),
     (dict(N=1 << 24, d=64), 2), (dict(N=1 << 23, d=128, dtype=1), 2), (dict(N=(1 << 22) + 64, d=128, dtype=0), 2),
-    (dict(d=32), 3), (dict(d=96), 3), (dict(d=512), 3), (dict(d=256, dtype=0), 3),
+    (dict(d=32, dtype=0), 3), (dict(d=96, dtype=0), 3), (dict(d=512), 3), (dict(d=256, dtype=0), 3),
+    (dict(d=48), 3), (dict(d=80), 3),
     (dict(dtype=2), 4), (dict(dtype=-1), 4),
     (dict(scale=0.0), 5), (dict(scale=-0.125), 5), (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5),
     (dict(q=P + 8), 6), (dict(o=P + 2), 6), (dict(lse=P + 4), 6),
@@ -188,7 +189,9 @@ def test_workspace_size():
     assert fa.fa_bwd_workspace_size(4, 16, 2048, 64, 1) == 2 * 4 * 16 * 2048 * 4
     assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 1) == 256
     assert fa.fa_bwd_workspace_size(1, 1, 3, 64, 0) == 0   # fp32 backward unsupported
-    assert fa.fa_bwd_workspace_size(1, 1, 3, 96, 1) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 96, 1) == 256   # head dims 32 and 96: bf16
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 32, 0) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 80, 1) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 3, 256, 1) == 256  # head dim 256: bf16 backward too
     assert fa.fa_bwd_workspace_size(1, 1, 3, 256, 0) == 0
     assert fa.fa_bwd_workspace_size(0, 1, 3, 64, 1) == 0

@@ -219,6 +219,24 @@ def test_bwd_d256(causal):
     check_bwd_heads(q, k, v, do, causal, 256 ** -0.5, [(0, h) for h in range(4)], "d256 B1 H4 N1024")
 
 
+@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims_32_96(d, causal):
+    """Head dims 32 (64-byte rows) and 96 (rows padded to 128 columns in LDS), bf16:
+    ragged forward sweep, backward on ragged lengths, then B=2 H=4 N=1024 on every head."""
+    need_gpu()
+    for i, N in enumerate(SWEEP_N):
+        q, k, v = inputs.gen_qkv((1 + i % 2, 1 + i % 3, N, d), "bf16", 1500 + 7 * i + d)
+        check_fwd_full(q, k, v, causal, d ** -0.5, "bf16", f"d{d} sweep N={N}")
+    for i, N in enumerate([1, 65, 129, 300]):
+        q, k, v, do = inputs.gen_qkv((1, 2, N, d), "bf16", 1600 + 7 * i + d, with_do=True)
+        check_bwd_heads(q, k, v, do, causal, d ** -0.5, [(0, 0), (0, 1)], f"d{d} bwd N={N}")
+    q, k, v, do = inputs.gen_qkv((2, 4, 1024, d), "bf16", 1650 + d + causal, with_do=True)
+    check_fwd_full(q, k, v, causal, d ** -0.5, "bf16", f"d{d} B2 H4 N1024")
+    check_bwd_heads(q, k, v, do, causal, d ** -0.5, [(b, h) for b in range(2) for h in range(4)],
+                    f"d{d} B2 H4 N1024")
+
+
 # ------------------------------------------------------------------ shared K/V heads
 
 def _gqa_check(case_name, heads_b0):
@@ -275,7 +293,7 @@ def test_mqa_d64():
     _gqa_check("mqa_b2hq16hkv1n1024d64", [0])
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa_sweep(d, causal):
     """Ragged lengths and group sizes 1..4 against the oracle on every head (dK and dV
