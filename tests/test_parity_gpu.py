@@ -237,6 +237,49 @@ def test_head_dims_32_96(d, causal):
                     f"d{d} B2 H4 N1024")
 
 
+def test_max_head_slab_d256():
+    """The largest head slab the ABI accepts (N*d*2 bytes just under 2^31: d = 256,
+    N = 2^22 - 64, causal), so 32-bit buffer offsets reach their limit.  The oracle
+    cannot hold these rows, so the inputs are built with a known answer: every key
+    row is the same vector, every visible key then has the same score, and
+    O_i = mean(V_0..V_i), lse_i = s q_i.k + ln(i + 1) exactly.  Checked on sampled
+    rows (first, around powers of two, last) against float64 prefix sums."""
+    need_gpu()
+    N, d = (1 << 22) - 64, 256
+    assert N * d * 2 < (1 << 31) and (N + 64) * d * 2 >= (1 << 31)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    q = torch.randn((1, 1, N, d), device="cuda", generator=g).to(torch.bfloat16)
+    krow = torch.randn((d,), device="cuda", generator=g).to(torch.bfloat16)
+    k = krow.expand(1, 1, N, d).contiguous()
+    v = torch.randn((1, 1, N, d), device="cuda", generator=g).to(torch.bfloat16)
+    scale = d ** -0.5
+    say(f"[fwd] max head slab N={N} d={d} causal ({N * d * 2} bytes per tensor)")
+    o, lse = fa.forward(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 2, 63, 64, 65, 4095, 4096, (1 << 20) - 1, 1 << 20, (1 << 21) + 5, N - 65, N - 2, N - 1})
+    # float64 prefix sums of V at the sampled rows, accumulated in chunks of 2^20 rows
+    pref = {}
+    run = torch.zeros(d, dtype=torch.float64, device="cuda")
+    step = 1 << 20
+    for c0 in range(0, N, step):
+        blk = v[0, 0, c0:c0 + step].double()
+        cs = torch.cumsum(blk, dim=0) + run
+        for r in rows:
+            if c0 <= r < c0 + step:
+                pref[r] = cs[r - c0].clone()
+        run = cs[-1].clone()
+        del blk, cs
+    s = f32(scale)
+    got_o = host(o[0, 0, rows])
+    got_l = host(lse[0, 0, rows])
+    ref_o = np.stack([(pref[r] / (r + 1)).cpu().numpy() for r in rows])
+    qk = (q[0, 0, rows].double() @ krow.double()).cpu().numpy()
+    ref_l = s * qk + np.log(np.asarray(rows, dtype=np.float64) + 1.0)
+    eo = assert_close("max slab O rows", got_o, ref_o, "bf16")
+    el = assert_close("max slab lse rows", got_l, ref_l, "bf16", lse=True)
+    say(f"   O max/rel {eo[0]:.2e}/{eo[1]:.2e}  lse max {el[0]:.2e}")
+
+
 # ------------------------------------------------------------------ shared K/V heads
 
 def _gqa_check(case_name, heads_b0):
