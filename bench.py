@@ -19,7 +19,8 @@ N(0,1) (seeded PCG64, rounded to bf16).
 Throughput counts 4*B*H*N^2*d flops for the forward (halved when causal) and
 2.5x that for the backward, i.e. the minimum matrix-product work; value =
 (forward + backward flops) / step time.  Per-kernel durations come from HIP
-events recorded on the stream the kernels run on.  The CPU baseline times the
+events recorded on the stream the kernels run on; fwd_ms_cold / bwd_ms_cold
+repeat each launch after a 512 MiB fill that evicts L2 and the Infinity Cache.  The CPU baseline times the
 float64 oracle on a bounded sample of heads of the same workload.
 Prints ONE JSON line.
 """
@@ -51,6 +52,9 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_bwd_encoder_b4h16n4096d128_
 BWD_SOURCES = ["exact_io_aware_49_amd/csrc/fa_bwd_bf16.hip", "exact_io_aware_49_amd/csrc/fa_device.h"]
 FP8_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_fwd_fp8_b4h16n4096d128_hbm_traffic.md")
 FP8_SOURCES = ["exact_io_aware_49_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_49_amd/csrc/fa_device.h"]
+DEC_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_b16hq32hkv8nk8192d128_kernel_trace.md")
+DEC_SOURCES = ["exact_io_aware_49_amd/csrc/fa_decode.hip", "exact_io_aware_49_amd/csrc/fa_device.h",
+               "exact_io_aware_49_amd/csrc/fa_internal.h"]
 
 
 def sources_sha(paths):
@@ -286,7 +290,9 @@ def decode_main(a, name):
         "config": {"workload": name, "B": B, "Hq": hq, "Hkv": hkv, "Nq": nq, "Nk": nk, "d": d,
                    "causal": bool(c["causal"]), "cache_rows": int(lens.sum())},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(DEC_TRAFFIC_PROFILE, DEC_SOURCES)
+                     if name == "decode_b16hq32hkv8nk8192d128" else None,
                      "kernel": "fa_decode (fa_decode_kernel + fa_decode_merge_kernel)",
                      "avg_launch_ms": round(launch_ms, 4)},
         "cpu_baseline": None,
@@ -391,6 +397,23 @@ def main(argv=None):
 
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    # cold caches (reported beside the warm figures, not part of `value`): a 512 MiB
+    # fill evicts L2 and the 256 MB Infinity Cache before each timed launch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = {"fwd": [], "bwd": []}
+    for _ in range(5):
+        for name, fn in (("fwd", fwd), ("bwd", bwd)):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold[name].append(e0.elapsed_time(e1))
+    del flush
+    fwd_ms_cold = float(np.median(cold["fwd"]))
+    bwd_ms_cold = float(np.median(cold["bwd"]))
     ms_per_step = wall * 1e3 / a.steps
     ff = fwd_flops(B, H, N, d, w.causal)
     bf = 2.5 * ff
@@ -427,6 +450,8 @@ def main(argv=None):
                    "causal": bool(w.causal), "scale": scale, **({"Hkv": hkv} if hkv != H else {})},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        "fwd_ms_cold": round(fwd_ms_cold, 4),
+        "bwd_ms_cold": round(bwd_ms_cold, 4),
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
         "bwd_tflops": round(bwd_tf, 2),
