@@ -14,7 +14,8 @@
 // wave per SIMD or for a second LDS fragment set, so that instantiation runs
 // one wave per SIMD and reads each chunk's fragments just before use.
 //
-// Mapping to one workgroup (4 waves, 256 threads), BR = 128 query rows:
+// Mapping to one workgroup (4 waves and BR = 128 query rows; 8 waves and BR =
+// 256 at d = 96 and 128, where one K/V tile then serves twice the rows):
 //   * Each wave owns 32 query rows.  Its Q rows sit in VGPRs as the B operand
 //     of S^T = K Q^T (lane = query row, 8 consecutive head-dim slots per lane).
 //   * A K/V tile of BC = 64 keys goes from HBM
@@ -51,7 +52,10 @@ namespace {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BR = 128;                    // query rows per workgroup
+  // waves per workgroup: 8 at d = 96 and 128 (one K/V tile in LDS serves 256
+  // query rows, about 3% faster than 4 waves), 4 otherwise
+  static constexpr int NWV = (D == 96 || D == 128) ? 8 : 4;
+  static constexpr int BR = 32 * NWV;               // query rows per workgroup
   static constexpr int BC = 64;                     // keys per tile
   static constexpr int NKT = BC / 32;               // 32-key score tiles per K/V tile
   static constexpr int KSTEPS = D / 16;             // MFMA k-steps over the head dim
@@ -64,13 +68,13 @@ struct FwdCfg {
   static constexpr int GROW_BYTES = D * 2;          // bytes per row in global memory
   static constexpr int RPI = 1024 / ROW_BYTES;      // rows per wave-wide 16-byte load
   static constexpr int TILE_BYTES = BC * ROW_BYTES;
-  static constexpr int LPW = TILE_BYTES / 1024 / 4; // loads per wave per tensor per tile
+  static constexpr int LPW = TILE_BYTES / 1024 / NWV; // loads per wave per tensor per tile
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 };
 
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, (D == 256) ? 1 : 2)
+__global__ void __launch_bounds__(64 * FwdCfg<D>::NWV, (D == 256) ? 1 : 8 / FwdCfg<D>::NWV)
 fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE,
                    int N, int nbh, int group, float scale_log2e) {
@@ -365,7 +369,7 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
   const int nqb = (N + C::BR - 1) / C::BR;
   const long long blocks = (long long)nqb * nbh;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(64 * C::NWV), 0, stream,
                      (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, N, nbh, group,
                      scale * kLog2e);
   return hipGetLastError();
