@@ -167,8 +167,11 @@ __device__ __forceinline__ void store_rows_bf16(__bf16 *row, const floatx16 (&ac
 }
 
 // ============================================================== dQ kernel
+// waves per dQ workgroup: 8 at d = 128 (one K/V tile in LDS serves 256 query rows,
+// 1-2% faster than 4), 4 otherwise
+template <int D> constexpr int dq_waves() { return (D == 128) ? 8 : 4; }
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, (D == 256) ? 1 : 2)
+__global__ void __launch_bounds__(64 * dq_waves<D>(), (D == 256) ? 1 : 8 / dq_waves<D>())
 fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                  const __bf16 *__restrict__ Og, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
                  __bf16 *__restrict__ dQ, float *__restrict__ Dsum, float *__restrict__ Lse2, int N,
@@ -176,7 +179,8 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
   using C = BwdCfg<D>;
   constexpr int TB = C::TB;
   constexpr int RB = C::RB;
-  constexpr int BR = 128;  // query rows per workgroup
+  constexpr int NW = dq_waves<D>();
+  constexpr int BR = 32 * NW;  // query rows per workgroup
   // LDS: K tiles at [0, TB), [TB, 2TB); V tiles at [2TB, 3TB), [3TB, 4TB)
   __shared__ __align__(1024) unsigned char smem[4 * TB];
 
@@ -241,8 +245,8 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
     wait_vmem();
     __syncthreads();  // tile t is in LDS for everyone; tile t-1 is no longer read
     if (t + 1 < ntiles) {
-      issue_tile<D>(krs, smem + (BUF ^ 1) * TB, (t + 1) * 64, wave, lane);
-      issue_tile<D>(vrs, smem + (2 + (BUF ^ 1)) * TB, (t + 1) * 64, wave, lane);
+      issue_tile<D, NW>(krs, smem + (BUF ^ 1) * TB, (t + 1) * 64, wave, lane);
+      issue_tile<D, NW>(vrs, smem + (2 + (BUF ^ 1)) * TB, (t + 1) * 64, wave, lane);
     }
     const int kb = t * 64;
     if (CAUSAL && kb > qw0 + 31) return;  // every key of the tile is above this wave's rows
@@ -288,8 +292,8 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
     });
   };
 
-  issue_tile<D>(krs, smem, 0, wave, lane);
-  issue_tile<D>(vrs, smem + 2 * TB, 0, wave, lane);
+  issue_tile<D, NW>(krs, smem, 0, wave, lane);
+  issue_tile<D, NW>(vrs, smem + 2 * TB, 0, wave, lane);
   for (int t = 0; t < ntiles; t += 2) {
     step(std::integral_constant<int, 0>{}, t);
     if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
@@ -702,14 +706,14 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
   const long long nbh = (long long)B * H;          // query heads
   const long long nkvh = nbh / group;              // K/V heads
   const int nsplit = bwd_splits(nkvh, N, group);
-  const long long gq = nbh * ((N + 127) / 128);
+  const long long gq = nbh * ((N + 32 * dq_waves<D>() - 1) / (32 * dq_waves<D>()));
   const long long gk = nkvh * nsplit * ((N + 127) / 128);
   if (gq > 0x7fffffffLL || gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const float c = scale * kLog2e;
   float *dsum = ws;
   float *lse2 = ws + (size_t)nbh * N;
   float *part = (nsplit > 1) ? ws + bwd_partial_offset_floats(nbh, N) : nullptr;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)gq), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)gq), dim3(64 * dq_waves<D>()), 0, stream,
                      (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)o,
                      (const __bf16 *)dout, lse, (__bf16 *)dq, dsum, lse2, N, group, c, scale);
   hipError_t e = hipGetLastError();
