@@ -202,6 +202,11 @@ def test_torch_api_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(RuntimeError):
         fa.forward(q, q, q)
+    with pytest.raises(RuntimeError):
+        fa.decode(q.to(torch.bfloat16), q.to(torch.bfloat16), q.to(torch.bfloat16))
+    c = torch.zeros(1, 1, 8, 64, dtype=torch.uint8)
+    with pytest.raises(RuntimeError):
+        fa.forward_fp8(c, c, c, 1.0, 1.0, 1.0)
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
