@@ -73,7 +73,7 @@ const char *fa_status_string(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a required pointer is NULL";
     case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H and N must be >= 1, the tensor size must fit, and the query heads must split evenly over the K/V heads";
-    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM: head dim d must be 64 or 128 (32, 96, 256: bf16 forward and backward only)";
+    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM: head dim d must be 64 or 128 (also 32, 96, 256 for the bf16 forward and backward, 256 for the FP8 forward)";
     case FA_ERR_UNSUPPORTED_DTYPE: return "FA_ERR_UNSUPPORTED_DTYPE: dtype not supported by this entry point";
     case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite and > 0";
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: tensor pointers must be 16-byte aligned";
@@ -112,7 +112,7 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, float q_scale, float
   int st = check_common(B, Hq, N, d, causal, scale, FA_DTYPE_BF16);
   if (st == FA_OK) st = check_heads(Hq, Hkv);
   if (st != FA_OK) return st;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED_HEAD_DIM;
   for (float x : {q_scale, k_scale, v_scale})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_BAD_SCALE;
   const float c = q_scale * k_scale * scale;

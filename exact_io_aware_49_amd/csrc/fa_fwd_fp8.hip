@@ -83,7 +83,7 @@ struct Fp8Cfg {
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, (D == 256) ? 1 : 2)
 fa_fwd_fp8_kernel(const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, const uint8_t *__restrict__ V,
                   __bf16 *__restrict__ O, float *__restrict__ LSE, int N, int nbh, int group, float score_log2e,
                   float v_scale) {
@@ -316,6 +316,9 @@ hipError_t launch(const void *q, const void *k, const void *v, float q_scale, fl
 hipError_t launch_fwd_fp8(const void *q, const void *k, const void *v, float q_scale, float k_scale, float v_scale,
                           void *o, float *lse, int B, int H, int group, int N, int d, bool causal, float scale,
                           hipStream_t stream) {
+  if (d == 256)
+    return causal ? launch<256, true>(q, k, v, q_scale, k_scale, v_scale, o, lse, B, H, group, N, scale, stream)
+                  : launch<256, false>(q, k, v, q_scale, k_scale, v_scale, o, lse, B, H, group, N, scale, stream);
   if (d == 64)
     return causal ? launch<64, true>(q, k, v, q_scale, k_scale, v_scale, o, lse, B, H, group, N, scale, stream)
                   : launch<64, false>(q, k, v, q_scale, k_scale, v_scale, o, lse, B, H, group, N, scale, stream);

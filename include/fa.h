@@ -32,8 +32,8 @@
  *    Masked scores get probability exactly 0.
  *  - scale must be finite and > 0 (the pages' value is 1/sqrt(d)).
  *  - Supported: d in {64, 128}, and d in {32, 96, 256} in bf16 (fa_fwd, fa_bwd
- *    and their _gqa forms; the fp32 forward, fa_decode and fa_fwd_fp8 return
- *    FA_ERR_UNSUPPORTED_HEAD_DIM for them);
+ *    and their _gqa forms); fa_fwd_fp8 takes d in {64, 128, 256}; the fp32
+ *    forward and fa_decode return FA_ERR_UNSUPPORTED_HEAD_DIM for other d;
  *    B, H, N >= 1; B*H*N*d < 2^62; one head's N*d elements below 2^31 bytes
  *    (N < 8,388,608 for bf16 at d = 128).
  */
@@ -61,7 +61,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL_POINTER = 1,         /* a required pointer is NULL */
   FA_ERR_BAD_SHAPE = 2,            /* B, H or N < 1, the element count overflows, or Hq % Hkv != 0 */
-  FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128} (32, 96, 256: bf16 forward and backward only) */
+  FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not supported by this entry point (see "Supported" above) */
   FA_ERR_UNSUPPORTED_DTYPE = 4,    /* dtype unknown, or not supported by this entry point */
   FA_ERR_BAD_SCALE = 5,            /* scale not finite or not > 0 */
   FA_ERR_MISALIGNED = 6,           /* a tensor pointer is not 16-byte aligned */
@@ -199,7 +199,7 @@ FA_API int fa_decode(const void *q, const void *k, const void *v, const int *kv_
  * combination of rows of V with weights within that rounding of the exact
  * ones.  q_scale, k_scale, v_scale must be finite and > 0, and
  * q_scale * k_scale * scale must stay a normal float (FA_ERR_BAD_SCALE).
- * d in {64, 128}.  Everything else is as for fa_fwd_gqa.
+ * d in {64, 128, 256}.  Everything else is as for fa_fwd_gqa.
  */
 FA_API int fa_fwd_fp8(const void *q, const void *k, const void *v,
                float q_scale, float k_scale, float v_scale, void *o, float *lse,

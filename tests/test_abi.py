@@ -176,7 +176,7 @@ def fp8(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(lse=None), 1),
     (dict(B=0), 2), (dict(N=0), 2), (dict(Hkv=3), 2), (dict(Hkv=0), 2),
-    (dict(d=256), 3), (dict(d=96), 3),
+    (dict(d=32), 3), (dict(d=96), 3), (dict(d=512), 3),
     (dict(scale=0.0), 5), (dict(qs=0.0), 5), (dict(ks=-1.0), 5), (dict(vs=float("inf")), 5),
     (dict(qs=float("nan")), 5), (dict(qs=1e-20, ks=1e-20), 5), (dict(qs=1e30, ks=1e30), 5),
     (dict(q=P + 8), 6), (dict(k=P + 1), 6), (dict(lse=P + 4), 6), (dict(causal=-1), 8),

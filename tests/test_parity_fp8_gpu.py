@@ -105,7 +105,7 @@ def check_fp8(q8, k8, v8, sc, causal, tag, heads=None, rows_per_head=None, seed=
     return worst
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_sweep(d, causal):
     # ragged N over several query blocks and key tiles, two query heads per K/V head
