@@ -18,12 +18,14 @@
 //     all-ones operand by P^T, so every lane holds its row's sum.
 //   * The contraction index of an MFMA is any fixed byte order shared by its
 //     two operands.  The key order of one 64-key step is the order in which
-//     the score accumulators hold their keys (tile k: 16 (t / 8) + 8 h + t % 8
-//     for byte t of lane half h), so P packs straight from the accumulators
+//     the score accumulators hold their keys (byte t of lane half h is key
+//     16 (t / 8) + 8 h + t % 8 of the tile), so P packs straight from the accumulators
 //     and V^T is read from the row-major tile with ds_read_b64_tr_b8 (a lane
 //     gets one column of 8 consecutive rows).
 //   * LDS operand reads are ordinary loads (and the tr8 builtin), so the
 //     compiler counts them and may move them ahead of their use.
+//   * d = 256 runs one wave per SIMD (its 32 x 256 output accumulator lives in
+//     AGPRs); d = 64 and 128 run two.
 #include "fa_device.h"
 #include "fa_internal.h"
 
