@@ -114,6 +114,14 @@ def test_fp8_sweep(d, causal):
     assert worst[2] < 0.05
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_mqa(d):
+    # multi-query: eight query heads over one K/V head, ragged N, causal and not
+    (q8, k8, v8), sc = inputs.gen_fp8((2, 8, 301, d), 960 + d, (2, 1, 301, d))
+    for causal in (False, True):
+        check_fp8(q8, k8, v8, sc, causal, f"mqa d{d} causal{int(causal)}", heads=[(0, 0), (0, 7), (1, 3)])
+
+
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 128, 129, 200])
 def test_fp8_small_and_ragged(N):
     (q8, k8, v8), sc = inputs.gen_fp8((1, 2, N, 128), 950 + N, (1, 1, N, 128))
