@@ -427,6 +427,28 @@ def test_forward_and_backward_are_deterministic():
         assert torch.equal(a, b)
 
 
+def test_gqa_decode_fp8_are_deterministic():
+    """Shared-K/V-head backward (split partials + fixed-order reduction), decode (fixed-order
+    merge) and the FP8 forward are bitwise reproducible run to run."""
+    need_gpu()
+    q, k, v, do = (dev(x, "bf16") for x in inputs.gen_gqa(1, 8, 2, 300, 128, "bf16", 82, with_do=True))
+    o, lse = fa.forward(q, k, v, causal=True)
+    g1 = fa.backward(q, k, v, o, do, lse, causal=True)
+    g2 = fa.backward(q, k, v, o, do, lse, causal=True)
+    qd, kd, vd, lens = inputs.gen_decode(4, 8, 2, 1, 2000, 128, 83, min_len=300)
+    td = [dev(x, "bf16") for x in (qd, kd, vd)]
+    ld = torch.from_numpy(lens).to("cuda")
+    d1 = fa.decode(td[0], td[1], td[2], ld)
+    d2 = fa.decode(td[0], td[1], td[2], ld)
+    (q8, k8, v8), sc = inputs.gen_fp8((1, 4, 300, 128), 84, (1, 2, 300, 128))
+    t8 = [torch.from_numpy(x).to("cuda") for x in (q8, k8, v8)]
+    f1 = fa.forward_fp8(t8[0], t8[1], t8[2], *sc, causal=True)
+    f2 = fa.forward_fp8(t8[0], t8[1], t8[2], *sc, causal=True)
+    torch.cuda.synchronize()
+    for a, b in list(zip(g1, g2)) + list(zip(d1, d2)) + list(zip(f1, f2)):
+        assert torch.equal(a, b)
+
+
 def test_golden_rational_case_fp32():
     """The hand-derived closed form of tests/golden, run through the fp32 GPU path (d padded to 64)."""
     need_gpu()
