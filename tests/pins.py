@@ -406,6 +406,20 @@ def pin_e4m3_codes():
     return out
 
 
+def pin_e4m3_matches_torch():
+    """Every E4M3 code decodes to the value torch's float8_e4m3fn gives it (a library routine
+    written independently of the oracle)."""
+    import torch
+    out = []
+    codes = np.arange(256, dtype=np.uint8)
+    ours = A.e4m3_to_float(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    bad = np.nonzero(~same)[0]
+    _fail_if(bad.size != 0, f"e4m3 codes differing from torch: {[hex(int(b)) for b in bad[:8]]}", out)
+    return out
+
+
 def pin_fp8_forward_is_forward_of_decoded():
     """The FP8 forward equals the plain forward of the decoded, scaled inputs (brute force)."""
     out = []
@@ -511,6 +525,7 @@ ALL_PINS = [
     pin_decode_brute_force,
     pin_decode_reduces_to_forward,
     pin_e4m3_codes,
+    pin_e4m3_matches_torch,
     pin_fp8_forward_is_forward_of_decoded,
 ]
 

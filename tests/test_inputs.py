@@ -78,3 +78,16 @@ def test_e4m3_encoder_round_trip():
     for xv, qv in zip(np.abs(x[:500]), np.abs(q[:500])):
         best = grid[np.argmin(np.abs(grid - min(xv, 448.0)))]
         assert abs(min(xv, 448.0) - qv) <= abs(min(xv, 448.0) - best) + 1e-12
+
+
+def test_e4m3_encoder_matches_torch_rounding():
+    """Within the finite range the FP8 input encoder rounds like torch's float8_e4m3fn
+    conversion (round to nearest even), code for code."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(8))
+    x = np.concatenate([(rng.standard_normal(20000) * s).astype(np.float32) for s in (0.01, 1.0, 40.0)])
+    x = x[np.abs(x) <= 448.0]
+    ours = inputs.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    same = (ours == ref) | ((ours & 0x7F) == 0) & ((ref & 0x7F) == 0)  # signed zeros
+    assert same.all(), [(float(a), int(b), int(c)) for a, b, c in zip(x[~same][:5], ours[~same][:5], ref[~same][:5])]
