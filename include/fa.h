@@ -28,7 +28,8 @@
  *    FA_ERR_HIP.  Nothing is printed; no exception crosses the ABI; the
  *    library holds no mutable global state, so calls are thread-safe.
  *  - causal = 1 applies the causal mask: query i sees key j iff j <= i
- *    (positions counted from 0; queries and keys have the same length N).
+ *    (positions counted from 0; queries and keys have the same length N;
+ *    fa_decode places its queries at the end of each cache, see there).
  *    Masked scores get probability exactly 0.
  *  - scale must be finite and > 0 (the pages' value is 1/sqrt(d)).
  *  - Supported: d in {64, 128}, and d in {32, 96, 256} in bf16 (fa_fwd, fa_bwd
