@@ -229,8 +229,39 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     }
   };
 
+  // Masked row maximum of one tile's scores, both halves of the wave combined.
+  // Diagonal and ragged tiles get -inf at the keys a row must not see.
+  auto tile_max = [&](floatx16 (&s)[C::NKT], int t) -> float {
+    const int kb = t * C::BC;
+    const bool need_mask = (CAUSAL && (kb + C::BC - 1 > qw0)) || (kb + C::BC > N);
+    if (need_mask) {
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 32 * kt + 16 * (r >> 3) + 8 * half + (r & 7);
+          if ((key >= N) || (CAUSAL && key > my_q)) s[kt][r] = -INFINITY;
+        }
+    }
+    float mloc = max3f(s[0][0], s[0][1], s[0][2]);
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int r = (kt == 0 ? 3 : 0); r < 16; r += 2) {
+        if (r + 1 < 16) mloc = max3f(mloc, s[kt][r], s[kt][r + 1]);
+        else mloc = fmaxf(mloc, s[kt][r]);
+      }
+    return max_with_partner(mloc);
+  };
+  // At d = 64, 96 and 256 the maximum of tile t+1 is taken at the end of step t,
+  // while that step's last matrix products still run, instead of after the
+  // barrier that starts step t+1, where every wave of a SIMD would do it at
+  // once with the matrix cores idle (1-4% faster there; at d = 32 and 128 no
+  // gain).  mt carries it from one step to the next.
+  constexpr bool EARLY_MAX = (D == 64 || D == 96 || D == 256);
+
   // One tile step.  BUF is the V buffer of tile t (and the K buffer of tile t).
-  auto step = [&](auto bufc, int t, floatx16 (&cur)[C::NKT], floatx16 (&nxt)[C::NKT]) {
+  auto step = [&](auto bufc, int t, floatx16 (&cur)[C::NKT], floatx16 (&nxt)[C::NKT], float &mt) {
     constexpr int BUF = decltype(bufc)::value;
     wait_vmem();
     __syncthreads();  // K(t+1) and V(t) are in LDS; nobody reads K(t) or V(t-1) any more
@@ -247,27 +278,8 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     if (AHEAD && act) read_frag(bufc, std::integral_constant<int, 0>{}, fa);
     float mc = 0.f;
     if (act) {
-      // ---- masking (diagonal and ragged tiles only)
-      const bool need_mask = (CAUSAL && (kb + C::BC - 1 > qw0)) || (kb + C::BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb + 32 * kt + 16 * (r >> 3) + 8 * half + (r & 7);
-            if ((key >= N) || (CAUSAL && key > my_q)) cur[kt][r] = -INFINITY;
-          }
-      }
-      // ---- row maximum of tile t
-      float mloc = max3f(cur[0][0], cur[0][1], cur[0][2]);
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-        for (int r = (kt == 0 ? 3 : 0); r < 16; r += 2) {
-          if (r + 1 < 16) mloc = max3f(mloc, cur[kt][r], cur[kt][r + 1]);
-          else mloc = fmaxf(mloc, cur[kt][r]);
-        }
-      const float m_tile = max_with_partner(mloc);
+      // ---- row maximum of tile t (masked)
+      const float m_tile = EARLY_MAX ? mt : tile_max(cur, t);
       const float m_new = fmaxf(m_ref, m_tile);
       // ---- move the reference maximum only when the scores outgrow it by > 2^8
       const bool grow = (m_new - m_ref) * scale_log2e > 8.0f;
@@ -321,6 +333,10 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
           oacc[ct] = mfma32x32x16(as_bf16x8(av), pb, oacc[ct]);
         }
       });
+      if constexpr (EARLY_MAX) {
+        const bool act1 = (t + 1 < ntiles) && (!CAUSAL || ((t + 1) * C::BC <= qw0 + 31));
+        if (act1) mt = tile_max(nxt, t + 1);
+      }
     }
   };
 
@@ -337,9 +353,11 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     qk_steps(sA[kt], smem, kt, 0, C::KSTEPS);
   }
 
+  float mt = 0.f;
+  if constexpr (EARLY_MAX) mt = tile_max(sA, 0);
   for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t, sA, sB);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1, sB, sA);
+    step(std::integral_constant<int, 0>{}, t, sA, sB, mt);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1, sB, sA, mt);
   }
 
   // ---- epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
