@@ -50,6 +50,14 @@
 namespace fa {
 namespace {
 
+// A causal d = 64 launch splits each workgroup's key range (SPLIT below) when
+// it would otherwise have at most this many 128-row workgroups, i.e. no more
+// than one per CU: there the unsplit launch runs one wave per SIMD through
+// the longest blocks' 16+ key tiles.  Measured: B2 H3 N1000 15.6 -> 10.3 us;
+// at 384 and more workgroups (B4/B8 H12 N1024) the split's 64 KB of LDS per
+// workgroup (2 per CU instead of 3) costs more than it saves (B8: 25 -> 31 us).
+constexpr long long SPLIT_MAX_WG = 256;
+
 template <int D>
 struct FwdCfg {
   // waves per workgroup: 8 at d = 96 and 128 (one K/V tile in LDS serves 256
@@ -73,16 +81,28 @@ struct FwdCfg {
 };
 
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(64 * FwdCfg<D>::NWV, (D == 256) ? 1 : 8 / FwdCfg<D>::NWV)
+// SPLIT (causal d = 64 launches with few workgroups): a workgroup owns 64 query
+// rows; waves 0-1 (one per 32 rows) take the lower half of the key tiles the
+// rows see and waves 2-3 the upper half, each pair with its own LDS buffers, and
+// the two partial results are merged at the end by the online-softmax rule
+// (m = max(m0, m1), O and l rescaled by 2^((m_i - m) c)).  The last query blocks
+// of a causal launch walk every key tile; splitting their keys halves that
+// sequential chain when there are too few workgroups to hide it.
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ void __launch_bounds__(64 * FwdCfg<D>::NWV, SPLIT ? 2 : ((D == 256) ? 1 : 8 / FwdCfg<D>::NWV))
 fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE,
                    int N, int nbh, int group, float scale_log2e) {
   using C = FwdCfg<D>;
+  static_assert(!SPLIT || (CAUSAL && C::NWV == 4), "the key split is built for 4-wave causal launches");
   constexpr int TB = C::TILE_BYTES;
   constexpr int RB = C::ROW_BYTES;
-  // LDS: K buffers at [0, TB) and [TB, 2TB), V buffers at [2TB, 3TB) and [3TB, 4TB)
-  __shared__ __align__(1024) unsigned char smem[4 * TB];
+  constexpr int RG = SPLIT ? 2 : C::NWV;              // waves along the query rows
+  constexpr int BRW = 32 * RG;                        // query rows per workgroup
+  constexpr int LPW = C::TILE_BYTES / 1024 / RG;      // loads per wave per tensor per tile
+  // LDS: K buffers at [0, TB) and [TB, 2TB), V buffers at [2TB, 3TB) and [3TB, 4TB);
+  // with SPLIT a second such set at [4TB, 8TB) for the upper key half
+  __shared__ __align__(1024) unsigned char smem[(SPLIT ? 8 : 4) * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,7 +110,11 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const int nqb = (N + C::BR - 1) / C::BR;
+  const int rg = SPLIT ? (wave & 1) : wave;  // 32-row group of this wave
+  const int kh = SPLIT ? (wave >> 1) : 0;    // key half of this wave
+  const int hb = kh * 4 * TB;                // LDS buffers of that key half
+
+  const int nqb = (N + BRW - 1) / BRW;
   int bh, qb;
   map_block(blockIdx.x, nqb, nbh, CAUSAL, bh, qb);
 
@@ -100,8 +124,8 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_off, head_bytes);
 
-  const int q0 = qb * C::BR;       // first query row of the workgroup
-  const int qw0 = q0 + wave * 32;  // first query row of this wave
+  const int q0 = qb * BRW;         // first query row of the workgroup
+  const int qw0 = q0 + rg * 32;    // first query row of this wave
   const int my_q = qw0 + l32;      // this lane's query row
 
   // ---- Q fragments: B operand, lane = query row, slots = d in [16*ks + 8*half, +8)
@@ -116,7 +140,11 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   // ---- number of key tiles this workgroup visits
   const int ntiles_all = (N + C::BC - 1) / C::BC;
   int ntiles = ntiles_all;
-  if (CAUSAL) ntiles = min(ntiles_all, (min(q0 + C::BR, N) - 1) / C::BC + 1);
+  if (CAUSAL) ntiles = min(ntiles_all, (min(q0 + BRW, N) - 1) / C::BC + 1);
+  // key tiles [t_lo, t_hi) of this wave's key half, visited in nsteps steps
+  const int nsteps = SPLIT ? (ntiles + 1) / 2 : ntiles;
+  const int t_lo = kh * nsteps;
+  const int t_hi = SPLIT ? (kh ? ntiles : nsteps) : ntiles;
 
   // ---- direct loads: wave w fills rows [(w*LPW + u)*RPI, +RPI) of a tile
   const int ld_row_in = lane / C::CPR;
@@ -130,18 +158,18 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   };
   auto issue_k = [&](int t, int lds_off) {
 #pragma unroll
-    for (int u = 0; u < C::LPW; ++u) {
-      const int row0 = (wave * C::LPW + u) * C::RPI;
+    for (int u = 0; u < LPW; ++u) {
+      const int row0 = (rg * LPW + u) * C::RPI;
       const int row = row0 + ld_row_in;
-      load_lds16(krs, smem + lds_off + row0 * RB, goff(t * C::BC + row, ld_chunk ^ swz_k<C::DL>(row)));
+      load_lds16(krs, smem + hb + lds_off + row0 * RB, goff(t * C::BC + row, ld_chunk ^ swz_k<C::DL>(row)));
     }
   };
   auto issue_v = [&](int t, int lds_off) {
 #pragma unroll
-    for (int u = 0; u < C::LPW; ++u) {
-      const int row0 = (wave * C::LPW + u) * C::RPI;
+    for (int u = 0; u < LPW; ++u) {
+      const int row0 = (rg * LPW + u) * C::RPI;
       const int row = row0 + ld_row_in;
-      load_lds16(vrs, smem + lds_off + row0 * RB, goff(t * C::BC + row, ld_chunk ^ swz_v<C::DL>(row)));
+      load_lds16(vrs, smem + hb + lds_off + row0 * RB, goff(t * C::BC + row, ld_chunk ^ swz_v<C::DL>(row)));
     }
   };
 
@@ -158,7 +186,7 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   // addresses row key0 + (j >> 2), columns 32*ct + 16*((l >> 4) & 1) + 4*(j & 3)
   uint32_t voff[C::CT][2];
   {
-    const uint32_t vb = lds_addr(smem) + 2 * TB;
+    const uint32_t vb = lds_addr(smem) + hb + 2 * TB;
     const int rlo = 8 * half + ((lane & 15) >> 2);
     const int tq = lane & 3;
 #pragma unroll
@@ -198,7 +226,7 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     u32x4 k[QK_PER_CH];
     u32x2 v[C::CT][2];
   };
-  const uint32_t kbase = lds_addr(smem);
+  const uint32_t kbase = lds_addr(smem) + hb;
   uint32_t kaddr[C::KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < C::KSTEPS; ++ks) kaddr[ks] = kbase + koff[ks];
@@ -265,8 +293,8 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     constexpr int BUF = decltype(bufc)::value;
     wait_vmem();
     __syncthreads();  // K(t+1) and V(t) are in LDS; nobody reads K(t) or V(t-1) any more
-    if (t + 2 < ntiles) issue_k(t + 2, BUF * TB);
-    if (t + 1 < ntiles) issue_v(t + 1, (2 + (BUF ^ 1)) * TB);
+    if (t + 2 < t_hi) issue_k(t + 2, BUF * TB);
+    if (t + 1 < t_hi) issue_v(t + 1, (2 + (BUF ^ 1)) * TB);
 
     const int kb = t * C::BC;
     const bool act = !CAUSAL || (kb <= qw0 + 31);
@@ -334,30 +362,63 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
         }
       });
       if constexpr (EARLY_MAX) {
-        const bool act1 = (t + 1 < ntiles) && (!CAUSAL || ((t + 1) * C::BC <= qw0 + 31));
+        const bool act1 = (t + 1 < t_hi) && (!CAUSAL || ((t + 1) * C::BC <= qw0 + 31));
         if (act1) mt = tile_max(nxt, t + 1);
       }
     }
   };
 
-  // ---- prologue: K(0), V(0), K(1) in flight, then S of tile 0
-  issue_k(0, 0);
-  issue_v(0, 2 * TB);
-  if (ntiles > 1) issue_k(1, TB);
+  // ---- prologue: K(t_lo), V(t_lo), K(t_lo+1) in flight, then S of tile t_lo
+  // (an empty upper key half -- a block that sees one tile -- loads nothing)
+  if (t_lo < t_hi) {
+    issue_k(t_lo, 0);
+    issue_v(t_lo, 2 * TB);
+  }
+  if (t_lo + 1 < t_hi) issue_k(t_lo + 1, TB);
   floatx16 sA[C::NKT], sB[C::NKT];
   wait_vmem();
   __syncthreads();
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt) {
     sA[kt] = floatx16{0};
-    qk_steps(sA[kt], smem, kt, 0, C::KSTEPS);
+    qk_steps(sA[kt], smem + hb, kt, 0, C::KSTEPS);
   }
 
   float mt = 0.f;
-  if constexpr (EARLY_MAX) mt = tile_max(sA, 0);
-  for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t, sA, sB, mt);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1, sB, sA, mt);
+  if constexpr (EARLY_MAX) mt = tile_max(sA, t_lo);
+  // (tiles at or past t_hi are above the diagonal of every row here, so the
+  // causal test in step() leaves them inactive)
+  for (int s = 0; s < nsteps; s += 2) {
+    step(std::integral_constant<int, 0>{}, t_lo + s, sA, sB, mt);
+    if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, t_lo + s + 1, sB, sA, mt);
+  }
+
+  if constexpr (SPLIT) {
+    // ---- merge the upper key half into the lower one: per lane its running
+    // maximum, exponential sum and O^T registers, through LDS
+    constexpr int XF = 2 + 16 * C::CT;  // floats per lane
+    float *xs = reinterpret_cast<float *>(smem) + rg * XF * 64;
+    __syncthreads();  // every wave is done reading K/V tiles
+    if (kh == 1) {
+      xs[lane] = m_ref;
+      xs[64 + lane] = l_part;
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[(2 + 16 * ct + r) * 64 + lane] = oacc[ct][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = xs[lane];
+    const float m = fmaxf(m_ref, m1);
+    const float a0 = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m) * scale_log2e);
+    const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2((m1 - m) * scale_log2e);
+    l_part = a0 * l_part + a1 * xs[64 + lane];
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[ct][r] = a0 * oacc[ct][r] + a1 * xs[(2 + 16 * ct + r) * 64 + lane];
+    if (m != -INFINITY) m_ref = m;
   }
 
   // ---- epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
@@ -379,15 +440,16 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT = false>
 hipError_t launch(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int group,
                   int N, float scale, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int nbh = B * H;
-  const int nqb = (N + C::BR - 1) / C::BR;
+  const int br = SPLIT ? 64 : C::BR;
+  const int nqb = (N + br - 1) / br;
   const long long blocks = (long long)nqb * nbh;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(64 * C::NWV), 0, stream,
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3((unsigned)blocks), dim3(64 * C::NWV), 0, stream,
                      (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, N, nbh, group,
                      scale * kLog2e);
   return hipGetLastError();
@@ -401,8 +463,12 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
                              : launch<96, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
   if (d == 32) return causal ? launch<32, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
                              : launch<32, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
-  if (d == 64) return causal ? launch<64, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
-                             : launch<64, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
+  if (d == 64) {
+    if (!causal) return launch<64, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
+    const long long wg128 = (long long)B * H * ((N + 127) / 128);
+    if (wg128 <= SPLIT_MAX_WG) return launch<64, true, true>(q, k, v, o, lse, B, H, group, N, scale, stream);
+    return launch<64, true>(q, k, v, o, lse, B, H, group, N, scale, stream);
+  }
   if (d == 256) return causal ? launch<256, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
                               : launch<256, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
   return causal ? launch<128, true>(q, k, v, o, lse, B, H, group, N, scale, stream)

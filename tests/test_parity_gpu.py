@@ -374,6 +374,23 @@ def test_fwd_sweep(dtype, d, causal):
         check_fwd_full(q, k, v, causal, d ** -0.5, dtype, f"sweep N={N}")
 
 
+def test_fwd_d64_causal_key_split():
+    """Causal d = 64 launches with at most 256 workgroups of 128 rows split each workgroup's
+    key range over two wave pairs and merge the two partial results.  Odd and even tile
+    counts, a block with an empty upper half (N <= 64), ragged ends, peaky scores (scale x4),
+    and one launch just above the threshold (unsplit) for contrast."""
+    need_gpu()
+    cases = [((1, 2, 1000), 1.0), ((2, 3, 1000), 1.0), ((1, 1, 2047), 1.0), ((1, 2, 64), 1.0),
+             ((1, 1, 65), 1.0), ((2, 2, 1500), 4.0), ((1, 1, 4096), 4.0)]
+    for i, ((B, H, N), mult) in enumerate(cases):
+        q, k, v = inputs.gen_qkv((B, H, N, 64), "bf16", 2100 + 5 * i)
+        check_fwd_full(q, k, v, True, mult * 0.125, "bf16", f"key split B={B} H={H} N={N} scale x{mult}",
+                       stress=mult != 1.0)
+    # 257 workgroups of 128 rows: the unsplit kernel
+    q, k, v = inputs.gen_qkv((1, 257, 128, 64), "bf16", 2190)
+    check_fwd_full(q, k, v, True, 0.125, "bf16", "unsplit B=1 H=257 N=128")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_sweep(d, causal):
