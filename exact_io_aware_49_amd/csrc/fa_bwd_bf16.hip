@@ -269,6 +269,15 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
           dp = mfma32x32x16(b[ks], dof[ks], dp);
         }
       }
+      // masked keys get a score of -inf, so P = 2^-inf = 0 exactly; done as a
+      // pass of its own so the exponentials below stay one branch-free block
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 32 * KT + 16 * (r >> 3) + 8 * half + (r & 7);
+          if (key >= N || (CAUSAL && key > my_q)) s[r] = -INFINITY;
+        }
+      }
       static_for<2>([&](auto mc) {
         constexpr int M = decltype(mc)::value;
         u32x4 w;
@@ -278,11 +287,7 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int r = 8 * M + 2 * i + e;
-            float p = fast_exp2(__builtin_fmaf(s[r], scale_log2e, -lse2));
-            if (need_mask) {
-              const int key = kb + 32 * KT + 16 * M + 8 * half + 2 * i + e;
-              if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
-            }
+            const float p = fast_exp2(__builtin_fmaf(s[r], scale_log2e, -lse2));
             d2[e] = p * (dp[r] - drow);
           }
           w[i] = pack_bf16x2(d2[0], d2[1]);
@@ -409,6 +414,15 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
           if constexpr (DO_K) dp = mfma32x32x16(b[i], vf[k0 + i], dp);
         }
       }
+      // masked (query, key) pairs get a score of -inf, so P = 0 exactly; a pass
+      // of its own keeps the exponentials below one branch-free block
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = qs + 32 * QT + 16 * (r >> 3) + 8 * half + (r & 7);
+          if (q >= N || !k_ok || (CAUSAL && q < my_k)) s[r] = -INFINITY;
+        }
+      }
       static_for<2>([&](auto mc) {
         constexpr int M = decltype(mc)::value;
         const int qoff = 32 * QT + 16 * M + 8 * half;  // tile-local query of register 8M
@@ -428,11 +442,7 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
             const int j = 2 * i + e;
             const float lq = (j < 4) ? l0[j] : l1[j - 4];
             const float dq = (j < 4) ? d0[j] : d1[j - 4];
-            float p = fast_exp2(__builtin_fmaf(s[8 * M + j], scale_log2e, -lq));
-            if (need_mask) {
-              const int q = qs + qoff + j;
-              if (q >= N || !k_ok || (CAUSAL && q < my_k)) p = 0.f;
-            }
+            const float p = fast_exp2(__builtin_fmaf(s[8 * M + j], scale_log2e, -lq));
             p2[e] = p;
             s2[e] = p * (dp[8 * M + j] - dq);
           }
@@ -575,6 +585,17 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
     }
     u32x4 pw[2][2];  // role 0: P of (sub-tile, half) as bf16, lane = key, 8 queries
     if (role == 0 && active) {
+      // masked (query, key) pairs get a score of -inf, so P = 0 exactly; a pass
+      // of its own keeps the exponentials below one branch-free block
+      if (need_mask) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = qs + 32 * qt + 16 * (r >> 3) + 8 * half + (r & 7);
+            if (q >= N || !k_ok || (CAUSAL && q < my_k)) first[qt][r] = -INFINITY;
+          }
+      }
       static_for<2>([&](auto qtc) {
         constexpr int QT = decltype(qtc)::value;
         static_for<2>([&](auto mc) {
@@ -590,11 +611,7 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
             for (int e = 0; e < 2; ++e) {
               const int j = 2 * i + e;
               const float lq = (j < 4) ? l0[j] : l1[j - 4];
-              float p = fast_exp2(__builtin_fmaf(first[QT][8 * M + j], scale_log2e, -lq));
-              if (need_mask) {
-                const int q = qs + qoff + j;
-                if (q >= N || !k_ok || (CAUSAL && q < my_k)) p = 0.f;
-              }
+              const float p = fast_exp2(__builtin_fmaf(first[QT][8 * M + j], scale_log2e, -lq));
               p2[e] = p;
               pf[j] = p;
             }
