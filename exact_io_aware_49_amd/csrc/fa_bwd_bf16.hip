@@ -540,8 +540,10 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
   const int g0 = (int)((long long)split * group / nsplit);
   const int g1 = (int)((long long)(split + 1) * group / nsplit);
   __amdgpu_buffer_rsrc_t qrs, ors, lrs, drs;  // the current query head's Q, dO, lse*log2e, D
+  // transposed reads of the second products: the dO tile (role 0, dV^T += dO^T P)
+  // or the Q tile (role 1, dK^T += Q^T dS), which is TB before it
   TileOffsets<D> to;
-  to.init(lane, lds_addr(smem));  // transposed reads of the Q tile; the dO tile is TB further
+  to.init(lane, lds_addr(smem) + (role == 0 ? TB : 0));
 
   auto issue = [&](int t, int stage) {
     unsigned char *base = smem + stage * STAGE;
@@ -626,15 +628,15 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
     }
     __syncthreads();  // P of every key group is in LDS
     if (!active) return;
+    // B operands of the second products: P (role 0) or dS (role 1).  Only these
+    // differ between the roles; the products themselves are one code path, so
+    // the accumulator is not copied where the two roles' branches meet.
+    u32x4 bop[2][2];
     if (role == 0) {
-      static_for<2>([&](auto qtc) {
-        constexpr int QT = decltype(qtc)::value;
-        static_for<2>([&](auto mc) {
-          constexpr int M = decltype(mc)::value;
-          constexpr int OFFQ = BUF * STAGE + 16 * (2 * QT + M) * RB;
-          mfma_transposed<D, OFFQ + TB>(acc, to, as_bf16x8(pw[QT][M]));  // dV^T += dO^T P
-        });
-      });
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) bop[qt][m] = pw[qt][m];
     } else {
       static_for<2>([&](auto qtc) {
         constexpr int QT = decltype(qtc)::value;
@@ -659,11 +661,19 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
             }
             sw[i] = pack_bf16x2(s2[0], s2[1]);
           }
-          constexpr int OFFQ = BUF * STAGE + 16 * (2 * QT + M) * RB;
-          mfma_transposed<D, OFFQ>(acc, to, as_bf16x8(sw));  // dK^T += Q^T dS
+          bop[QT][M] = sw;
         });
       });
     }
+    // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1)
+    static_for<2>([&](auto qtc) {
+      constexpr int QT = decltype(qtc)::value;
+      static_for<2>([&](auto mc) {
+        constexpr int M = decltype(mc)::value;
+        constexpr int OFFQ = BUF * STAGE + 16 * (2 * QT + M) * RB;
+        mfma_transposed<D, OFFQ>(acc, to, as_bf16x8(bop[QT][M]));
+      });
+    });
   };
 
   for (int g = g0; g < g1; ++g) {
