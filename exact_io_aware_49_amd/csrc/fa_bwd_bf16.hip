@@ -626,6 +626,21 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
         });
       });
     }
+    if (role == 1 && active) {
+      // dP - D now, while the partner still forms P: after the barrier the dS
+      // wave is the critical path and only has to multiply by P
+      static_for<2>([&](auto qtc) {
+        constexpr int QT = decltype(qtc)::value;
+        static_for<2>([&](auto mc) {
+          constexpr int M = decltype(mc)::value;
+          const int qoff = 32 * QT + 16 * M + 8 * half;
+          const floatx4 d0 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff);
+          const floatx4 d1 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) first[QT][8 * M + j] -= (j < 4) ? d0[j] : d1[j - 4];
+        });
+      });
+    }
     __syncthreads();  // P of every key group is in LDS
     if (!active) return;
     // B operands of the second products: P (role 0) or dS (role 1).  Only these
@@ -642,9 +657,6 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
         constexpr int QT = decltype(qtc)::value;
         static_for<2>([&](auto mc) {
           constexpr int M = decltype(mc)::value;
-          const int qoff = 32 * QT + 16 * M + 8 * half;
-          const floatx4 d0 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff);
-          const floatx4 d1 = *reinterpret_cast<const floatx4 *>(lst + 64 + qoff + 4);
           const unsigned char *slot = smem + PBUF + ((QT * 4 + kg) * 2 + M) * 2048 + lane * 16;
           const floatx4 p0 = *reinterpret_cast<const floatx4 *>(slot);
           const floatx4 p1 = *reinterpret_cast<const floatx4 *>(slot + 1024);
@@ -655,9 +667,8 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const int j = 2 * i + e;
-              const float dq = (j < 4) ? d0[j] : d1[j - 4];
               const float p = (j < 4) ? p0[j] : p1[j - 4];
-              s2[e] = p * (first[QT][8 * M + j] - dq);
+              s2[e] = p * first[QT][8 * M + j];  // P (dP - D)
             }
             sw[i] = pack_bf16x2(s2[0], s2[1]);
           }
