@@ -285,8 +285,33 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   // while that step's last matrix products still run, instead of after the
   // barrier that starts step t+1, where every wave of a SIMD would do it at
   // once with the matrix cores idle (1-4% faster there; at d = 32 and 128 no
-  // gain).  mt carries it from one step to the next.
+  // gain).  mt carries it to the next step.  At d = 256 the move of the
+  // reference maximum it may cause is made there too (REF_AT_TAIL).
   constexpr bool EARLY_MAX = (D == 64 || D == 96 || D == 256);
+  constexpr bool REF_AT_TAIL = (D == 256);
+
+  // Move the reference maximum only when a tile's scores outgrow it by more than
+  // 2^8 (in exp2 units); O and l are rescaled with it.
+  auto update_ref = [&](float m_tile) {
+    const float m_new = fmaxf(m_ref, m_tile);
+    const bool grow = (m_new - m_ref) * scale_log2e > 8.0f;
+    if (__ballot(grow) != 0) {
+      const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m_new) * scale_log2e);
+      m_ref = (m_new == -INFINITY) ? m_ref : m_new;
+      l_part *= alpha;
+      if constexpr (D == 256) {
+        // the accumulators live in AGPRs here; pinning them there at this point
+        // keeps the compiler from copying all of them to VGPRs on every step
+        // (outside this rarely taken branch) for the multiply below
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) asm volatile("" : "+a"(oacc[ct]));
+      }
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[ct][r] *= alpha;
+    }
+  };
 
   // One tile step.  BUF is the V buffer of tile t (and the K buffer of tile t).
   auto step = [&](auto bufc, int t, floatx16 (&cur)[C::NKT], floatx16 (&nxt)[C::NKT], float &mt) {
@@ -306,20 +331,9 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     if (AHEAD && act) read_frag(bufc, std::integral_constant<int, 0>{}, fa);
     float mc = 0.f;
     if (act) {
-      // ---- row maximum of tile t (masked)
-      const float m_tile = EARLY_MAX ? mt : tile_max(cur, t);
-      const float m_new = fmaxf(m_ref, m_tile);
-      // ---- move the reference maximum only when the scores outgrow it by > 2^8
-      const bool grow = (m_new - m_ref) * scale_log2e > 8.0f;
-      if (__ballot(grow) != 0) {
-        const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m_new) * scale_log2e);
-        m_ref = (m_new == -INFINITY) ? m_ref : m_new;
-        l_part *= alpha;
-#pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[ct][r] *= alpha;
-      }
+      // ---- row maximum of tile t (masked) and the reference maximum
+      if constexpr (!EARLY_MAX) update_ref(tile_max(cur, t));
+      else if constexpr (!REF_AT_TAIL) update_ref(mt);
       mc = (m_ref == -INFINITY) ? 0.f : m_ref * scale_log2e;
     }
 
@@ -363,7 +377,10 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
       });
       if constexpr (EARLY_MAX) {
         const bool act1 = (t + 1 < t_hi) && (!CAUSAL || ((t + 1) * C::BC <= qw0 + 31));
-        if (act1) mt = tile_max(nxt, t + 1);
+        if (act1) {
+          mt = tile_max(nxt, t + 1);
+          if constexpr (REF_AT_TAIL) update_ref(mt);
+        }
       }
     }
   };
@@ -385,7 +402,10 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   }
 
   float mt = 0.f;
-  if constexpr (EARLY_MAX) mt = tile_max(sA, t_lo);
+  if constexpr (EARLY_MAX) {
+    mt = tile_max(sA, t_lo);
+    if constexpr (REF_AT_TAIL) update_ref(mt);
+  }
   // (tiles at or past t_hi are above the diagonal of every row here, so the
   // causal test in step() leaves them inactive)
   for (int s = 0; s < nsteps; s += 2) {
