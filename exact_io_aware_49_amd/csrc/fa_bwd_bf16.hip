@@ -9,12 +9,12 @@
 //   dS = P (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Two kernels, no atomics:
-//   fa_bwd_dq_kernel   -- owns 128 query rows (32 per wave).  Computes D for its
+//   fa_bwd_dq_kernel   -- owns 128 query rows (256 at d = 128; 32 per wave).  Computes D for its
 //                         rows and stores D and lse*log2(e) for the second kernel,
 //                         then streams K/V tiles of 64 keys:
 //                         S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
 //                         Lane = query row, so lse and D are per-lane scalars.
-//   fa_bwd_dkdv_kernel -- (d = 64) owns 128 keys (32 per wave), K and V rows
+//   fa_bwd_dkdv_kernel -- (d = 32, 64, 96, 256) owns 128 keys (32 per wave), K and V rows
 //                         held in registers.  Streams Q/dO tiles of 64 queries:
 //                         S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
 //                         Lane = key.
@@ -32,7 +32,11 @@
 // operand of the first products) and transposed (ds_read_b64_tr_b16, the A
 // operand of the second products).  P and dS go straight from the accumulator
 // registers of the first products into the B operand of the second ones (row
-// order fixed by swap_bits23), so they never touch LDS.
+// order fixed by swap_bits23); only the pair kernel also hands P (float32) to
+// the partner wave through LDS.  Masked scores are set to -inf in a pass before
+// the exponentials (P = 0 exactly), which keeps the exponential code one
+// branch-free block.  At d = 256 the one-wave kernel runs as two launches, one
+// for dV and one for dK (one wave cannot hold both accumulators there).
 #include "fa_device.h"
 #include "fa_internal.h"
 

@@ -9,7 +9,8 @@
 // exponential sum per row, and writes only O and lse.  The N x N scores never
 // leave registers.
 //
-// Head dims 64, 128 and 256.  At d = 256 a wave's Q fragments (64 registers),
+// Head dims 32, 64, 96, 128 and 256 (d = 96 in a 128-column LDS layout whose
+// last four chunks read as zero).  At d = 256 a wave's Q fragments (64 registers),
 // output accumulator (128) and two score tiles (64) leave no room for a second
 // wave per SIMD or for a second LDS fragment set, so that instantiation runs
 // one wave per SIMD and reads each chunk's fragments just before use.
