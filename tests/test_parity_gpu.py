@@ -404,10 +404,12 @@ def test_bwd_sweep(d, causal):
 # ------------------------------------------------------------------ stress / structure
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_growing_scores_force_rescale(causal):
-    """Scores that rise along the keys make the running maximum move on every tile."""
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+def test_growing_scores_force_rescale(causal, d):
+    """Scores that rise along the keys make the running maximum move on every tile (every head
+    dim: each places the rescale of the output accumulator differently)."""
     need_gpu()
-    N, d = 1024, 64
+    N = 1024
     q, k, v = inputs.gen_qkv((1, 2, N, d), "bf16", 77)
     ramp = np.linspace(0.0, 6.0, N, dtype=np.float32)
     q[..., 0] = 4.0
