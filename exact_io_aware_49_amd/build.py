@@ -50,10 +50,23 @@ def common_flags(debug: bool):
     return flags
 
 
+# Per-source code-generation flags.  The decode kernel runs one wave per SIMD,
+# where the compiler otherwise keeps its matrix accumulators in AGPRs and copies
+# all of them to VGPRs and back on every key tile; the VGPR form of the MFMA
+# instructions removes those copies (same results, 2-8% faster).
+SOURCE_FLAGS = {
+    "fa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
+def source_flags(src: str):
+    return list(SOURCE_FLAGS.get(os.path.basename(src), []))
+
+
 def compile_one(src: str, debug: bool) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags(debug) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags(debug) + source_flags(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

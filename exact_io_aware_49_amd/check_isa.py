@@ -91,7 +91,7 @@ def check_text(text: str, name: str = "<asm>"):
 def device_asm(src: str, outdir: str) -> str:
     """Compile one source to gfx950 assembly; return its path."""
     out = os.path.join(outdir, os.path.splitext(os.path.basename(src))[0] + ".s")
-    cmd = [B.hipcc()] + B.common_flags(False) + ["--offload-device-only", "-S", src, "-o", out]
+    cmd = [B.hipcc()] + B.common_flags(False) + B.source_flags(src) + ["--offload-device-only", "-S", src, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"assembly generation failed: {' '.join(cmd)}\n{r.stderr}")
