@@ -135,6 +135,9 @@ class _Case:
         self.name = name
         if name in inputs.WORKLOADS:
             w = inputs.WORKLOADS[name]
+            if w.dtype != "bf16":
+                raise SystemExit(f"{name} is a {w.dtype} forward-only parity case (the tests check it); "
+                                 "bench.py times bf16 forward+backward steps")
             self.B, self.H, self.N, self.d = w.shape
             self.hkv, self.causal, self.scale, self.seed = w.H, w.causal, w.scale, w.seed
         elif name in inputs.GQA_CASES:
