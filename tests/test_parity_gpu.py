@@ -374,6 +374,15 @@ def test_fwd_sweep(dtype, d, causal):
         check_fwd_full(q, k, v, causal, d ** -0.5, dtype, f"sweep N={N}")
 
 
+def test_fwd_f32_rows_per_wave():
+    """The float32 forward picks 1, 2 or 4 query rows per wave from the grid size; these launches
+    select 2 (B1 H4 N1000 d64, causal) and 4 (B2 H4 N1100 d128) rows per wave (the sweeps, 1)."""
+    need_gpu()
+    for (B, H, N, d, causal), seed in (((1, 4, 1000, 64, True), 2201), ((2, 4, 1100, 128, False), 2202)):
+        q, k, v = inputs.gen_qkv((B, H, N, d), "f32", seed)
+        check_fwd_full(q, k, v, causal, d ** -0.5, "f32", f"f32 B={B} H={H} N={N} d={d}")
+
+
 def test_fwd_d64_causal_key_split():
     """Causal d = 64 launches with at most 256 workgroups of 128 rows split each workgroup's
     key range over two wave pairs and merge the two partial results.  Odd and even tile
