@@ -32,8 +32,8 @@ STATUS_NAMES = {
     5: "FA_ERR_BAD_SCALE",
     6: "FA_ERR_MISALIGNED",
     7: "FA_ERR_WORKSPACE_TOO_SMALL",
-    8: "FA_ERR_BAD_ARGUMENT",
-    9: "FA_ERR_HIP",
+    8: "FA_ERR_HIP",
+    9: "FA_ERR_BAD_ARGUMENT",
 }
 
 _lib = None

@@ -67,8 +67,8 @@ typedef enum {
   FA_ERR_BAD_SCALE = 5,            /* scale not finite or not > 0 */
   FA_ERR_MISALIGNED = 6,           /* a tensor pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE_TOO_SMALL = 7,  /* workspace NULL or smaller than fa_bwd_workspace_size() */
-  FA_ERR_BAD_ARGUMENT = 8,         /* causal not 0 or 1 */
-  FA_ERR_HIP = 9                   /* a HIP launch or runtime call failed */
+  FA_ERR_HIP = 8,                  /* a HIP launch or runtime call failed */
+  FA_ERR_BAD_ARGUMENT = 9          /* causal not 0 or 1 (appended after the original eight codes) */
 } fa_status_t;
 
 /*
