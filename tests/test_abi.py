@@ -68,7 +68,7 @@ def bwd(**kw):
     (dict(dtype=2), 4), (dict(dtype=-1), 4),
     (dict(scale=0.0), 5), (dict(scale=-0.125), 5), (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5),
     (dict(q=P + 8), 6), (dict(o=P + 2), 6), (dict(lse=P + 4), 6),
-    (dict(causal=2), 8), (dict(causal=-1), 8),
+    (dict(causal=2), 9), (dict(causal=-1), 9),
 ])
 def test_fwd_validation(kw, code):
     assert fwd(**kw) == code
@@ -78,7 +78,7 @@ def test_fwd_validation(kw, code):
     (dict(do=None), 1), (dict(dq=None), 1), (dict(lse=None), 1),
     (dict(N=0), 2), (dict(d=80), 3), (dict(d=512), 3), (dict(dtype=0), 4), (dict(d=256, dtype=0), 3),
     (dict(scale=0.0), 5),
-    (dict(ws=None), 7), (dict(wsb=100), 7), (dict(dk=P + 8), 6), (dict(ws=P + 8), 6), (dict(causal=3), 8),
+    (dict(ws=None), 7), (dict(wsb=100), 7), (dict(dk=P + 8), 6), (dict(ws=P + 8), 6), (dict(causal=3), 9),
 ])
 def test_bwd_validation(kw, code):
     assert bwd(**kw) == code
@@ -103,7 +103,7 @@ def bwd_gqa(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(k=None), 1), (dict(Hkv=0), 2), (dict(Hkv=-2), 2), (dict(Hkv=3), 2), (dict(Hkv=16), 2),
     (dict(Hq=0), 2), (dict(d=80), 3), (dict(dtype=3), 4), (dict(scale=0.0), 5), (dict(v=P + 4), 6),
-    (dict(causal=2), 8),
+    (dict(causal=2), 9),
 ])
 def test_fwd_gqa_validation(kw, code):
     assert fwd_gqa(**kw) == code
@@ -147,7 +147,7 @@ def dec(**kw):
     (dict(B=0), 2), (dict(Nq=0), 2), (dict(Nk=0), 2), (dict(Hkv=3), 2), (dict(Hkv=0), 2),
     (dict(Nk=1 << 23), 2), (dict(d=256), 3), (dict(d=96), 3), (dict(dtype=0), 4),
     (dict(scale=0.0), 5), (dict(scale=float("nan")), 5), (dict(q=P + 8), 6), (dict(lens=P + 2), 6),
-    (dict(ws=P + 4), 6), (dict(ws=None), 7), (dict(wsb=1024), 7), (dict(causal=2), 8),
+    (dict(ws=P + 4), 6), (dict(ws=None), 7), (dict(wsb=1024), 7), (dict(causal=2), 9),
 ])
 def test_decode_validation(kw, code):
     assert dec(**kw) == code
@@ -179,7 +179,7 @@ def fp8(**kw):
     (dict(d=32), 3), (dict(d=96), 3), (dict(d=512), 3),
     (dict(scale=0.0), 5), (dict(qs=0.0), 5), (dict(ks=-1.0), 5), (dict(vs=float("inf")), 5),
     (dict(qs=float("nan")), 5), (dict(qs=1e-20, ks=1e-20), 5), (dict(qs=1e30, ks=1e30), 5),
-    (dict(q=P + 8), 6), (dict(k=P + 1), 6), (dict(lse=P + 4), 6), (dict(causal=-1), 8),
+    (dict(q=P + 8), 6), (dict(k=P + 1), 6), (dict(lse=P + 4), 6), (dict(causal=-1), 9),
 ])
 def test_fwd_fp8_validation(kw, code):
     assert fp8(**kw) == code
