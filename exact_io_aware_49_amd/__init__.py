@@ -13,6 +13,8 @@ from .fa import (  # noqa: F401
     fa_bwd,
     fa_bwd_gqa,
     fa_bwd_gqa_workspace_size,
+    fa_bwd_noalloc,
+    fa_bwd_noalloc_scratch_bytes,
     fa_bwd_workspace_size,
     fa_decode,
     fa_decode_workspace_size,

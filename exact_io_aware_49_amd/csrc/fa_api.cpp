@@ -7,7 +7,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_internal.h"
@@ -62,6 +64,36 @@ int check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, floa
   return FA_OK;
 }
 
+// ---- static scratch for fa_bwd_noalloc -----------------------------------
+// The backward's per-row workspace (D and lse * log2 e, two float32 per query
+// row) for callers that cannot allocate.  Every GPU the library runs on holds
+// its own copy of this array until the process ends.  Host code never passes
+// the array's name to a kernel: it is a host-side stand-in, not a device
+// address.  Its device address is looked up once per device with
+// hipGetSymbolAddress and kept in scratch_ptr.
+constexpr size_t kScratchBytes = size_t(16) << 20;  // 16 MiB: up to 2^21 query rows
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_ptr[kMaxDevices];
+std::mutex scratch_mutex;
+
+// Device address of `scratch` on the current device, or nullptr if the lookup
+// failed (or the device index is out of range).
+void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  p = scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,6 +112,7 @@ const char *fa_status_string(int status) {
     case FA_ERR_WORKSPACE_TOO_SMALL: return "FA_ERR_WORKSPACE_TOO_SMALL: workspace missing or below fa_bwd_workspace_size()";
     case FA_ERR_BAD_ARGUMENT: return "FA_ERR_BAD_ARGUMENT: causal must be 0 or 1";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch or runtime call failed";
+    case FA_ERR_SCRATCH_TOO_SMALL: return "FA_ERR_SCRATCH_TOO_SMALL: fa_bwd_noalloc needs more than its 16 MiB static scratch (B*H*N above 2^21)";
     default: return "unknown fa status code";
   }
 }
@@ -166,6 +199,27 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            int causal, float scale, int dtype, void *stream) {
   return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d, causal, scale,
                     dtype, stream);
+}
+
+size_t fa_bwd_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+                   void *dq, void *dk, void *dv, int B, int H, int N, int d, int causal, float scale, int dtype,
+                   void *stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
+  int st = check_common(B, H, N, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_MISALIGNED;
+  // one query head per K/V head: the workspace is D and lse * log2 e only
+  if (fa_bwd_gqa_workspace_size(B, H, H, N, d, dtype) > kScratchBytes) return FA_ERR_SCRATCH_TOO_SMALL;
+  void *ws = scratch_on_current_device();
+  if (!ws) return FA_ERR_HIP;
+  hipError_t e = fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, (float *)ws, B, H, 1, N, d, causal == 1,
+                                     scale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype) {

@@ -34,6 +34,7 @@ STATUS_NAMES = {
     7: "FA_ERR_WORKSPACE_TOO_SMALL",
     8: "FA_ERR_HIP",
     9: "FA_ERR_BAD_ARGUMENT",
+    10: "FA_ERR_SCRATCH_TOO_SMALL",
 }
 
 _lib = None
@@ -55,6 +56,10 @@ def load_library(path: str = LIB_PATH):
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_scratch_bytes.argtypes = []
+    lib.fa_bwd_noalloc_scratch_bytes.restype = sz
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_gqa.restype = i
     lib.fa_bwd_gqa_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -89,6 +94,15 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, 
            stream) -> int:
     return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                                  causal, scale, dtype, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype, stream) -> int:
+    return load_library().fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype,
+                                         stream)
+
+
+def fa_bwd_noalloc_scratch_bytes() -> int:
+    return load_library().fa_bwd_noalloc_scratch_bytes()
 
 
 def fa_fwd_gqa(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream) -> int:

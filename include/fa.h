@@ -68,7 +68,8 @@ typedef enum {
   FA_ERR_MISALIGNED = 6,           /* a tensor pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE_TOO_SMALL = 7,  /* workspace NULL or smaller than fa_bwd_workspace_size() */
   FA_ERR_HIP = 8,                  /* a HIP launch or runtime call failed */
-  FA_ERR_BAD_ARGUMENT = 9          /* causal not 0 or 1 (appended after the original eight codes) */
+  FA_ERR_BAD_ARGUMENT = 9,         /* causal not 0 or 1 (appended after the original eight codes) */
+  FA_ERR_SCRATCH_TOO_SMALL = 10    /* fa_bwd_noalloc: the problem needs more than the static scratch */
 } fa_status_t;
 
 /*
@@ -119,6 +120,28 @@ FA_API int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            void *workspace, size_t workspace_bytes,
            int B, int H, int N, int d, int causal, float scale, int dtype,
            void *stream);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results as fa_bwd, without the workspace arguments:
+ * the per-row workspace lives in a static device array of the library
+ * (fa_bwd_noalloc_scratch_bytes() = 16 MiB, which covers B*H*N up to 2^21
+ * query rows, e.g. B=1 H=32 N=65536).  Larger problems return
+ * FA_ERR_SCRATCH_TOO_SMALL and enqueue nothing.  The call allocates nothing
+ * (no hipMalloc, no library allocation); its first call on a device looks up
+ * that device's copy of the array once (hipGetSymbolAddress), and each device
+ * keeps its copy until the process ends.  The array is shared by every call on
+ * a device: calls that overlap on one device (on different streams, or from
+ * different threads without ordering) race and give undefined results.  The
+ * backward needs no part of it zeroed.  The current device must be the one
+ * that owns the tensors and the stream.
+ */
+FA_API int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                   const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                   int B, int H, int N, int d, int causal, float scale, int dtype,
+                   void *stream);
+FA_API size_t fa_bwd_noalloc_scratch_bytes(void);
 
 /*
  * Query heads sharing key/value heads (multi-query attention, which

@@ -29,7 +29,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_symbols()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_gqa", "fa_bwd_gqa",
                           "fa_bwd_gqa_workspace_size", "fa_decode", "fa_decode_workspace_size",
-                          "fa_fwd_fp8", "fa_status_string", "fa_version"}
+                          "fa_fwd_fp8", "fa_status_string", "fa_version", "fa_bwd_noalloc",
+                          "fa_bwd_noalloc_scratch_bytes"}
     for n in names:
         assert hasattr(lib, n), n
     raw = ctypes.CDLL(fa.LIB_PATH)
@@ -42,6 +43,18 @@ def test_status_strings_and_version():
         assert fa.fa_status_string(code).startswith(name)
     assert "unknown" in fa.fa_status_string(12345)
     assert fa.fa_version() == 10000
+
+
+def test_noalloc_validation_before_any_hip_call():
+    # the static scratch is 16 MiB: 2 floats per query row, so B*H*N <= 2^21
+    assert fa.fa_bwd_noalloc_scratch_bytes() == 16 << 20
+    big = (1 << 21) + 1
+    assert fa.fa_bwd_noalloc(P, P, P, P, P, P, P, P, P, 1, 1, big, 64, 0, 0.125, 1, None) == 10
+    assert fa.fa_bwd_noalloc(P, P, P, P, P, P, P, P, P, 2, 4, big // 8 + 1, 64, 0, 0.125, 1, None) == 10
+    assert fa.fa_bwd_noalloc(P, 0, P, P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.125, 1, None) == 1
+    assert fa.fa_bwd_noalloc(P, P, P, P, P, P, P, P, P, 1, 1, 128, 64, 2, 0.125, 1, None) == 9
+    assert fa.fa_bwd_noalloc(P, P, P, P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.125, 0, None) == 4
+    assert fa.fa_bwd_noalloc(P, P, P, P, P, P, P, P + 8, P, 1, 1, 128, 64, 0, 0.125, 1, None) == 6
 
 
 def fwd(**kw):
