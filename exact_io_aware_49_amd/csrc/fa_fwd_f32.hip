@@ -95,7 +95,7 @@ fa_fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K, cons
 
     if (CAUSAL && kb > qw0 + F_ROWS - 1) continue;  // whole tile above this wave's rows
 
-    // scores of key (kb + lane) against the wave's 16 rows
+    // scores of key (kb + lane) against the wave's F_ROWS (1, 2 or 4) rows
     float s[F_ROWS];
 #pragma unroll
     for (int i = 0; i < F_ROWS; ++i) s[i] = 0.f;

@@ -88,7 +88,100 @@ def test_workload_fwd_encoder():
 
 
 def test_workload_fwd_longctx_causal():
-    check_fwd_sampled(inputs.WORKLOADS["fwd_longctx_causal_b1h32n32768d128"], set(), 8)
+    """The 32K causal forward: heads 0 and 31 in full; on every head the first, a middle
+    and the last 256-row query block (one workgroup's rows each; the last one holds the
+    causal diagonal of the longest rows) plus sampled rows elsewhere."""
+    need_gpu()
+    w = inputs.WORKLOADS["fwd_longctx_causal_b1h32n32768d128"]
+    q, k, v = inputs.workload_inputs(w)
+    B, H, N, d = w.shape
+    say(f"[fwd] {w.name}: full heads 0 and {H - 1}; blocks 0, {N // 512}, {N // 256 - 1} of 256 rows on every head")
+    o, lse = run_fwd(q, k, v, w.causal, w.scale, w.dtype)
+    s = f32(w.scale)
+    worst_o, worst_l = [0.0, 0.0], 0.0
+    for h in (0, H - 1):
+        ro, rl = oracle.attention_forward(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], w.causal, s, row_chunk=512)
+        e = assert_close(f"{w.name} O[0,{h}]", o[0, h], ro[0, 0], w.dtype)
+        el = assert_close(f"{w.name} lse[0,{h}]", lse[0, h], rl[0, 0], w.dtype, lse=True)
+        worst_o = [max(worst_o[0], e[0]), max(worst_o[1], e[1])]
+        worst_l = max(worst_l, el[0])
+        say(f"   head {h} in full: O max/rel {e[0]:.2e}/{e[1]:.2e}  lse max {el[0]:.2e}")
+    rng = np.random.Generator(np.random.PCG64(1000 + w.seed))
+    blocks = (0, N // 512, N // 256 - 1)
+    for h in range(H):
+        rows = set(_sampled_rows(N, rng, 8).tolist())
+        for blk in blocks:
+            rows |= set(range(256 * blk, 256 * blk + 256))
+        rows = np.array(sorted(rows))
+        ro, rl = oracle.attention_forward_rows(q, k, v, w.causal, s, 0, h, rows)
+        e = assert_close(f"{w.name} O[0,{h}] blocks+rows", o[0, h, rows], ro, w.dtype)
+        el = assert_close(f"{w.name} lse[0,{h}] blocks+rows", lse[0, h, rows], rl, w.dtype, lse=True)
+        worst_o = [max(worst_o[0], e[0]), max(worst_o[1], e[1])]
+        worst_l = max(worst_l, el[0])
+    say(f"   worst O max/rel {worst_o[0]:.2e}/{worst_o[1]:.2e}  worst lse max {worst_l:.2e}")
+
+
+# ------------------------------------------------------------------ the two named C entry points, called raw
+
+def _raw_fwd(qd, kd, vd, causal, scale, dtype_code):
+    B, H, N, d = qd.shape
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=qd.device)
+    rc = fa.fa_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                   int(causal), scale, dtype_code, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, fa.fa_status_string(rc)
+    return o, lse
+
+
+def test_c_abi_fa_fwd_fp32_and_gpt2_workloads():
+    """fa_fwd itself (raw device pointers through ctypes) on the float32 workload
+    (B1 H2 N128 d64, 1e-5) and the GPT-2-shape causal bf16 workload, every output
+    element against the oracle."""
+    need_gpu()
+    for name, code in (("fwd_f32_b1h2n128d64", fa.FA_DTYPE_F32), ("fwd_gpt2_causal_b8h12n1024d64", fa.FA_DTYPE_BF16)):
+        w = inputs.WORKLOADS[name]
+        say(f"[fa_fwd raw] {w.name}")
+        q, k, v = inputs.workload_inputs(w)
+        o, lse = _raw_fwd(dev(q, w.dtype), dev(k, w.dtype), dev(v, w.dtype), w.causal, w.scale, code)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attention_forward(q, k, v, w.causal, f32(w.scale))
+        eo = assert_close(f"{w.name} O", host(o), ro, w.dtype)
+        el = assert_close(f"{w.name} lse", host(lse), rl, w.dtype, lse=True)
+        say(f"   O max/rel {eo[0]:.2e}/{eo[1]:.2e}  lse max {el[0]:.2e}")
+
+
+def test_c_abi_fa_bwd_causal_workload():
+    """fa_fwd then fa_bwd (raw pointers, caller-allocated workspace of
+    fa_bwd_workspace_size bytes) on the causal backward workload B4 H16 N2048 d64:
+    six heads in full against the oracle's gradients, identities on all heads."""
+    need_gpu()
+    w = inputs.WORKLOADS["bwd_causal_b4h16n2048d64"]
+    q, k, v, do = inputs.workload_inputs(w)
+    B, H, N, d = w.shape
+    say(f"[fa_bwd raw] {w.name}")
+    qd, kd, vd, dod = (dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = _raw_fwd(qd, kd, vd, w.causal, w.scale, fa.FA_DTYPE_BF16)
+    need = fa.fa_bwd_workspace_size(B, H, N, d, fa.FA_DTYPE_BF16)
+    assert need == 2 * B * H * N * 4
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    rc = fa.fa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), dod.data_ptr(), lse.data_ptr(),
+                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), need, B, H, N, d, int(w.causal),
+                   w.scale, fa.FA_DTYPE_BF16, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, fa.fa_status_string(rc)
+    torch.cuda.synchronize()
+    gq, gk, gv = host(dq), host(dk), host(dv)
+    s = f32(w.scale)
+    worst = {}
+    for (b, h) in [(0, 0), (0, 15), (1, 3), (2, 8), (3, 0), (3, 15)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], w.causal, s)
+        for name, got, ref in (("dQ", gq[b, h], rq[0, 0]), ("dK", gk[b, h], rk[0, 0]), ("dV", gv[b, h], rv[0, 0])):
+            e = assert_close(f"{w.name} {name}[{b},{h}]", got, ref, "bf16")
+            worst[name] = max(worst.get(name, (0, 0)), e)
+    assert np.abs(gk.sum(axis=2)).max() < 0.5
+    assert np.abs(gv.sum(axis=2) - do.astype(np.float64).sum(axis=2)).max() < 0.5
+    say("   worst " + "  ".join(f"{n} max/rel {e[0]:.2e}/{e[1]:.2e}" for n, e in worst.items()))
 
 
 def run_bwd(q, k, v, do, causal, scale, dtype="bf16"):
