@@ -1,6 +1,7 @@
 """Benchmark: one training step of exact attention (forward + backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --calibrate-copy     (HBM counter calibration: a plain 512 MiB copy, 3 times)
 
 --workload also accepts the shared-K/V-head cases (query heads grouped over
 fewer K/V heads), e.g. gqa_causal_b2hq32hkv4n2048d128; they are timed the same
@@ -84,20 +85,37 @@ def fwd_flops(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
-def _oracle_threads():
-    """Threads numpy's BLAS runs the oracle's matrix products with."""
+def host_info():
+    """The host the oracle runs on: usable cores, CPU model, and numpy's BLAS (vendor,
+    version, threads).  The oracle runs in this one process; its matrix products use
+    the BLAS threads, the rest of numpy one thread."""
+    usable = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", usable
     try:
         from threadpoolctl import threadpool_info
-        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+            threads = int(libs[0].get("num_threads", usable))
     except Exception:
-        return len(os.sched_getaffinity(0))
+        pass
+    return {"cores": threads, "usable_cores": usable, "cpu_model": model, "blas": blas,
+            "parallelism": f"one process; numpy BLAS on {threads} threads, elementwise numpy on one"}
 
 
 def cpu_baseline(w, budget_s: float):
     """Time the float64 oracle (forward + backward) on whole query heads until ~budget_s elapse."""
     import oracle
 
-    threads = _oracle_threads()
     B, H, N, d = w.shape
     q, k, v, do = w.inputs()
     g = H // k.shape[1]
@@ -120,7 +138,7 @@ def cpu_baseline(w, budget_s: float):
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        **host_info(),
         "kind": "oracle",
         "sample": f"{heads} of {B * H} query heads (B={B},H={H},N={N},d={d}), float64 numpy forward+backward, "
                   f"{dt:.1f} s wall",
@@ -239,7 +257,7 @@ def fp8_main(a, name):
                 break
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(fwd_flops(1, heads, N, d, causal) / dt / 1e12, 4),
-                                "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
+                                "unit": "TFLOP/s", **host_info(), "kind": "oracle",
                                 "sample": f"{heads} of {B * hq} query heads, float64 numpy forward of the "
                                           f"decoded inputs, {dt:.1f} s wall"}
     print(json.dumps(line), flush=True)
@@ -314,9 +332,24 @@ def decode_main(a, name):
                 break
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(2.0 * hkv * rows * d * 2 / dt / 1e9, 3), "unit": "GB/s",
-                                "cores": _oracle_threads(), "kind": "oracle",
+                                **host_info(), "kind": "oracle",
                                 "sample": f"{done} of {B} sequences, float64 numpy, {dt:.1f} s wall"}
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def calibrate_copy(mib: int = 512, reps: int = 3):
+    """A plain device-to-device copy of a known size, for scaling the HBM byte counters
+    (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE): each copy reads and writes exactly
+    mib MiB, so counter / true bytes is the factor the kernels' counts are divided by."""
+    import torch
+
+    a = torch.ones(mib * (1 << 20) // 2, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {mib} MiB x{reps}", flush=True)
     return 0
 
 
@@ -328,7 +361,11 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 512 MiB device copy three times (HBM counter calibration)")
     a = ap.parse_args(argv)
+    if a.calibrate_copy:
+        return calibrate_copy()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
