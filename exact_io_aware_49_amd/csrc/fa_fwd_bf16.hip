@@ -59,6 +59,10 @@ namespace {
 // workgroup (2 per CU instead of 3) costs more than it saves (B8: 25 -> 31 us).
 constexpr long long SPLIT_MAX_WG = 256;
 
+// Sequence lengths from which d = 128 launches use the 64-rows-per-wave kernel.
+constexpr int R64_MIN_N = 4096;
+constexpr int R64_MIN_N_CAUSAL = 16384;
+
 template <int D>
 struct FwdCfg {
   // waves per workgroup: 8 at d = 96 and 128 (one K/V tile in LDS serves 256
@@ -492,6 +496,12 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
   }
   if (d == 256) return causal ? launch<256, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
                               : launch<256, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
+  // d = 128, long sequences: the kernel with 64 query rows per wave (fa_fwd_bf16_r64.hip),
+  // 2-3% faster there; shorter and causal launches below 16K keep this kernel, whose
+  // finer 32-row waves balance the causal diagonal better (the other kernel is 3%
+  // slower at B2 H16 N4096 causal and at B8 H16 N1024)
+  if (causal ? (N >= R64_MIN_N_CAUSAL) : (N >= R64_MIN_N))
+    return launch_fwd_bf16_r64(q, k, v, o, lse, B, H, group, N, causal, scale, stream);
   return causal ? launch<128, true>(q, k, v, o, lse, B, H, group, N, scale, stream)
                 : launch<128, false>(q, k, v, o, lse, B, H, group, N, scale, stream);
 }

@@ -64,6 +64,8 @@ inline DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
 // query heads; `group` query heads share one K/V head (H / group K/V heads).
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                            int group, int N, int d, bool causal, float scale, hipStream_t stream);
+hipError_t launch_fwd_bf16_r64(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                               int group, int N, bool causal, float scale, hipStream_t stream);
 hipError_t launch_fwd_fp8(const void *q, const void *k, const void *v, float q_scale, float k_scale, float v_scale,
                           void *o, float *lse, int B, int H, int group, int N, int d, bool causal, float scale,
                           hipStream_t stream);

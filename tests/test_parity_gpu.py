@@ -522,6 +522,43 @@ def test_growing_scores_force_rescale(causal, d):
     check_bwd_heads(q, k, v, do, causal, 1.0, [(0, 0), (0, 1)], "growing scores", stress=True)
 
 
+def _check_fwd_chunked(q, k, v, causal, scale, tag, stress=False):
+    say(f"[fwd] {tag} shape={q.shape} kv heads={k.shape[1]} causal={causal}")
+    o, lse = run_fwd(q, k, v, causal, scale, "bf16")
+    ro, rl = oracle.attention_forward(q, k, v, causal, f32(scale), row_chunk=1024)
+    eo = assert_close(f"{tag} O", o, ro, "bf16", magnitude_scaled=stress)
+    el = assert_close(f"{tag} lse", lse, rl, "bf16", lse=True, magnitude_scaled=stress)
+    say(f"   O max/rel {eo[0]:.2e}/{eo[1]:.2e}  lse max {el[0]:.2e}")
+
+
+def test_fwd_d128_long_kernel_cases():
+    """Head dim 128 at N >= 4096 (non-causal) and N >= 16384 (causal) runs the kernel with 64
+    query rows per wave: ragged lengths (masked last tile, rows past N), shared K/V heads,
+    and the causal diagonal at 16K."""
+    need_gpu()
+    q, k, v = inputs.gen_qkv((1, 2, 4100, 128), "bf16", 90)
+    _check_fwd_chunked(q, k, v, False, 128 ** -0.5, "d128 N4100")
+    q, k, v = inputs.gen_gqa(1, 4, 2, 4096, 128, "bf16", 91)
+    _check_fwd_chunked(q, k, v, False, 128 ** -0.5, "d128 Hq4 Hkv2 N4096")
+    q, k, v = inputs.gen_qkv((1, 1, 16390, 128), "bf16", 92)
+    _check_fwd_chunked(q, k, v, True, 128 ** -0.5, "d128 N16390 causal")
+
+
+@pytest.mark.parametrize("causal,N", [(False, 4096), (True, 16384)])
+def test_fwd_d128_long_scores_outgrow_first_tile(causal, N):
+    """The 64-rows-per-wave kernel keeps tile 0's row maximum as its reference and moves it only
+    when a chunk's probabilities would pass 2^64: scores that rise by about 115 in exp2 units
+    along the keys force that move several times per row."""
+    need_gpu()
+    q, k, v = inputs.gen_qkv((1, 1, N, 128), "bf16", 93)
+    ramp = np.linspace(0.0, 20.0, N, dtype=np.float32)
+    q = inputs.bf16_round(q * 0.25)
+    q[..., 0] = 4.0  # score rise 4 * 20 = 80 (natural log units) along the keys
+    k[..., 0] = inputs.bf16_round(ramp)[None, None, :]
+    k = inputs.bf16_round(k)
+    _check_fwd_chunked(q, k, v, causal, 1.0, f"d128 N{N} rising scores", stress=True)
+
+
 def test_peaky_scale():
     need_gpu()
     q, k, v = inputs.gen_qkv((2, 2, 512, 128), "bf16", 79)
