@@ -12,8 +12,9 @@ in between (for example by inserting a register copy):
   * s_waitcnt with lgkmcnt(0) clears every pending register;
   * any other instruction that names a pending VGPR is a violation.
 
-The scan follows program order through the text, which is conservative across
-branches (a register stays pending until a later lgkmcnt(0) in the text).
+The scan follows the control-flow graph of each function (blocks split at labels
+and branches): a register is pending at the start of a block if it is pending at
+the end of any predecessor, so a wait on every path is required.
 
     python -m exact_io_aware_49_amd.check_isa [file.s ...]
 With no arguments the kernel sources are compiled to assembly first.
@@ -42,49 +43,122 @@ def regs_of(operands: str):
     return out
 
 
-def check_text(text: str, name: str = "<asm>"):
-    """Return a list of violation strings for one assembly file."""
-    violations = []
-    pending = {}  # vgpr -> line number of the asm read
+BRANCH_RE = re.compile(r"^s_(c?branch\w*|setpc_b64|endpgm\w*)$")
+
+
+def _functions(text: str):
+    """Split assembly text into functions: lists of (line, op, operands, in_asm) and labels."""
+    funcs = []
+    cur = None
     in_asm = False
-    func = None
     for ln, raw in enumerate(text.splitlines(), 1):
-        line = raw.split(";", 1)[0].rstrip() if not raw.lstrip().startswith(";;#ASM") else raw.strip()
-        if raw.strip().startswith(";;#ASMSTART"):
+        stripped = raw.strip()
+        if stripped.startswith(";;#ASMSTART"):
             in_asm = True
             continue
-        if raw.strip().startswith(";;#ASMEND"):
+        if stripped.startswith(";;#ASMEND"):
             in_asm = False
             continue
+        line = raw.split(";", 1)[0].rstrip()
         if not line.strip():
             continue
         if re.match(r"^[A-Za-z_.$][\w.$]*:", line):
             lab = line.split(":")[0]
             if not lab.startswith(".L"):
-                func = lab
-                pending.clear()
+                cur = {"name": lab, "insts": [], "labels": {}}
+                funcs.append(cur)
+            elif cur is not None:
+                cur["labels"][lab] = len(cur["insts"])
+            continue
+        if cur is None:
             continue
         parts = line.strip().split(None, 1)
         op = parts[0]
-        operands = parts[1] if len(parts) > 1 else ""
         if op.startswith("."):
             continue
-        if op == "s_waitcnt":
-            if re.search(r"lgkmcnt\(0\)", operands):
-                pending.clear()
-            continue
-        if in_asm and op.startswith("ds_read"):
-            dst = operands.split(",", 1)[0]
-            for r in regs_of(dst):
-                pending[r] = ln
-            continue
-        if in_asm:
-            continue
-        touched = regs_of(operands) & set(pending)
-        if touched:
-            violations.append(f"{name}:{ln}: {func}: '{line.strip()}' uses v{sorted(touched)} "
-                              f"loaded by the inline-asm LDS read at line {pending[min(touched)]} "
-                              f"before lgkmcnt(0)")
+        cur["insts"].append((ln, op, parts[1] if len(parts) > 1 else "", in_asm))
+    return funcs
+
+
+def _check_function(f, name):
+    """Data flow over the function's control-flow graph: a register read by an
+    inline-asm ds_read is pending until an s_waitcnt lgkmcnt(0) on every path;
+    any other instruction naming a pending register is a violation."""
+    insts, labels = f["insts"], f["labels"]
+    n = len(insts)
+    starts = sorted(set([0] + list(labels.values()) +
+                        [i + 1 for i, (_, op, _, _) in enumerate(insts) if BRANCH_RE.match(op)]))
+    starts = [b for b in starts if b < n]
+    block_of = {}
+    blocks = []
+    for bi, b in enumerate(starts):
+        e = starts[bi + 1] if bi + 1 < len(starts) else n
+        blocks.append((b, e))
+        block_of[b] = bi
+    succs = []
+    for bi, (b, e) in enumerate(blocks):
+        ln, op, operands, _ = insts[e - 1]
+        nxt = [bi + 1] if bi + 1 < len(blocks) else []
+        if op == "s_branch" or op.startswith("s_setpc") or op.startswith("s_endpgm"):
+            tgt = []
+            if op == "s_branch":
+                lab = operands.split()[0]
+                if lab in labels and labels[lab] in block_of:
+                    tgt = [block_of[labels[lab]]]
+            succs.append(tgt)
+        elif op.startswith("s_cbranch"):
+            lab = operands.split()[0]
+            tgt = [block_of[labels[lab]]] if lab in labels and labels[lab] in block_of else []
+            succs.append(tgt + nxt)
+        else:
+            succs.append(nxt)
+    pend_in = [dict() for _ in blocks]
+    violations = {}
+
+    def transfer(bi, pend):
+        pend = dict(pend)
+        b, e = blocks[bi]
+        for ln, op, operands, in_asm in insts[b:e]:
+            if op == "s_waitcnt":
+                if re.search(r"lgkmcnt\(0\)", operands):
+                    pend.clear()
+                continue
+            if in_asm and op.startswith("ds_read"):
+                for r in regs_of(operands.split(",", 1)[0]):
+                    pend[r] = ln
+                continue
+            if in_asm:
+                continue
+            touched = regs_of(operands) & set(pend)
+            if touched:
+                violations[ln] = (f"{name}:{ln}: {f['name']}: '{op} {operands}' uses v{sorted(touched)} "
+                                  f"loaded by the inline-asm LDS read at line {pend[min(touched)]} "
+                                  f"before lgkmcnt(0)")
+        return pend
+
+    work = list(range(len(blocks)))
+    while work:
+        bi = work.pop(0)
+        out = transfer(bi, pend_in[bi])
+        for sj in succs[bi]:
+            merged = dict(pend_in[sj])
+            changed = False
+            for r, l in out.items():
+                if r not in merged:
+                    merged[r] = l
+                    changed = True
+            if changed:
+                pend_in[sj] = merged
+                if sj not in work:
+                    work.append(sj)
+    return [violations[k] for k in sorted(violations)]
+
+
+def check_text(text: str, name: str = "<asm>"):
+    """Return a list of violation strings for one assembly file."""
+    violations = []
+    for f in _functions(text):
+        violations += _check_function(f, name)
     return violations
 
 

@@ -94,7 +94,7 @@ struct FwdCfg {
 // of a causal launch walk every key tile; splitting their keys halves that
 // sequential chain when there are too few workgroups to hide it.
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ void __launch_bounds__(64 * FwdCfg<D>::NWV, SPLIT ? 2 : ((D == 256) ? 1 : 8 / FwdCfg<D>::NWV))
+__global__ void __launch_bounds__(64 * FwdCfg<D>::NWV, SPLIT ? 2 : ((D == 256) ? 1 : (D == 64) ? 3 : 8 / FwdCfg<D>::NWV))
 fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE,
                    int N, int nbh, int group, float scale_log2e) {
@@ -286,6 +286,20 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
       }
     return max_with_partner(mloc);
   };
+  // Only the mask of tile_max (used while the reference stays at the first tile's maximum).
+  auto mask_only = [&](floatx16 (&s)[C::NKT], int t) {
+    const int kb = t * C::BC;
+    const bool need_mask = (CAUSAL && (kb + C::BC - 1 > qw0)) || (kb + C::BC > N);
+    if (need_mask) {
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 32 * kt + 16 * (r >> 3) + 8 * half + (r & 7);
+          if ((key >= N) || (CAUSAL && key > my_q)) s[kt][r] = -INFINITY;
+        }
+    }
+  };
   // At d = 64, 96 and 256 the maximum of tile t+1 is taken at the end of step t,
   // while that step's last matrix products still run, instead of after the
   // barrier that starts step t+1, where every wave of a SIMD would do it at
@@ -319,7 +333,8 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
   };
 
   // One tile step.  BUF is the V buffer of tile t (and the K buffer of tile t).
-  auto step = [&](auto bufc, int t, floatx16 (&cur)[C::NKT], floatx16 (&nxt)[C::NKT], float &mt) {
+  auto step = [&](auto fastc, auto bufc, int t, floatx16 (&cur)[C::NKT], floatx16 (&nxt)[C::NKT], float &mt) {
+    constexpr bool FAST = decltype(fastc)::value;
     constexpr int BUF = decltype(bufc)::value;
     wait_vmem();
     __syncthreads();  // K(t+1) and V(t) are in LDS; nobody reads K(t) or V(t-1) any more
@@ -336,9 +351,15 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
     if (AHEAD && act) read_frag(bufc, std::integral_constant<int, 0>{}, fa);
     float mc = 0.f;
     if (act) {
-      // ---- row maximum of tile t (masked) and the reference maximum
-      if constexpr (!EARLY_MAX) update_ref(tile_max(cur, t));
-      else if constexpr (!REF_AT_TAIL) update_ref(mt);
+      // ---- row maximum of tile t (masked) and the reference maximum; with FAST
+      // the reference stays at the first tile's maximum and only the mask is applied
+      if constexpr (FAST) {
+        if constexpr (!EARLY_MAX) mask_only(cur, t);
+      } else if constexpr (!EARLY_MAX) {
+        update_ref(tile_max(cur, t));
+      } else if constexpr (!REF_AT_TAIL) {
+        update_ref(mt);
+      }
       mc = (m_ref == -INFINITY) ? 0.f : m_ref * scale_log2e;
     }
 
@@ -383,39 +404,76 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
       if constexpr (EARLY_MAX) {
         const bool act1 = (t + 1 < t_hi) && (!CAUSAL || ((t + 1) * C::BC <= qw0 + 31));
         if (act1) {
-          mt = tile_max(nxt, t + 1);
-          if constexpr (REF_AT_TAIL) update_ref(mt);
+          if constexpr (FAST) {
+            mask_only(nxt, t + 1);
+          } else {
+            mt = tile_max(nxt, t + 1);
+            if constexpr (REF_AT_TAIL) update_ref(mt);
+          }
         }
       }
     }
   };
 
   // ---- prologue: K(t_lo), V(t_lo), K(t_lo+1) in flight, then S of tile t_lo
-  // (an empty upper key half -- a block that sees one tile -- loads nothing)
-  if (t_lo < t_hi) {
-    issue_k(t_lo, 0);
-    issue_v(t_lo, 2 * TB);
-  }
-  if (t_lo + 1 < t_hi) issue_k(t_lo + 1, TB);
+  // (an empty upper key half -- a block that sees one tile -- loads nothing).
+  // The loop runs first with FAST: the reference maximum is the first tile's
+  // row maximum and is never moved, so no later tile needs a row maximum
+  // (probabilities keep their relative precision at any magnitude; O and l share
+  // the reference).  If a row sum then exceeds 2^64 or O is not finite, the
+  // workgroup runs the loop again with the moving reference.  Key-split (SPLIT)
+  // launches, a few tiles per workgroup, use the moving reference directly.
   floatx16 sA[C::NKT], sB[C::NKT];
-  wait_vmem();
-  __syncthreads();
+  auto run = [&](auto fastc) {
+    constexpr bool FAST = decltype(fastc)::value;
 #pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt) {
-    sA[kt] = floatx16{0};
-    qk_steps(sA[kt], smem + hb, kt, 0, C::KSTEPS);
-  }
+    for (int ct = 0; ct < C::CT; ++ct) oacc[ct] = floatx16{0};
+    m_ref = -INFINITY;
+    l_part = 0.f;
+    if (t_lo < t_hi) {
+      issue_k(t_lo, 0);
+      issue_v(t_lo, 2 * TB);
+    }
+    if (t_lo + 1 < t_hi) issue_k(t_lo + 1, TB);
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt) {
+      sA[kt] = floatx16{0};
+      qk_steps(sA[kt], smem + hb, kt, 0, C::KSTEPS);
+    }
 
-  float mt = 0.f;
-  if constexpr (EARLY_MAX) {
-    mt = tile_max(sA, t_lo);
-    if constexpr (REF_AT_TAIL) update_ref(mt);
-  }
-  // (tiles at or past t_hi are above the diagonal of every row here, so the
-  // causal test in step() leaves them inactive)
-  for (int s = 0; s < nsteps; s += 2) {
-    step(std::integral_constant<int, 0>{}, t_lo + s, sA, sB, mt);
-    if (s + 1 < nsteps) step(std::integral_constant<int, 1>{}, t_lo + s + 1, sB, sA, mt);
+    float mt = 0.f;
+    if constexpr (FAST) {
+      update_ref(tile_max(sA, t_lo));
+    } else if constexpr (EARLY_MAX) {
+      mt = tile_max(sA, t_lo);
+      if constexpr (REF_AT_TAIL) update_ref(mt);
+    }
+    // (tiles at or past t_hi are above the diagonal of every row here, so the
+    // causal test in step() leaves them inactive)
+    for (int s = 0; s < nsteps; s += 2) {
+      step(fastc, std::integral_constant<int, 0>{}, t_lo + s, sA, sB, mt);
+      if (s + 1 < nsteps) step(fastc, std::integral_constant<int, 1>{}, t_lo + s + 1, sB, sA, mt);
+    }
+    // every LDS read of the loop was waited for inside its step; this wait makes
+    // that visible to the static check of the generated code, which scans it in
+    // text order (the loop's wait may be laid out before its last reads)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  if constexpr (SPLIT) {
+    // small launches (a few tiles per workgroup): the moving reference directly
+    run(std::false_type{});
+  } else {
+    run(std::true_type{});
+    float osum = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) osum += oacc[ct][r];
+    constexpr float kLMax = 18446744073709551616.f;  // 2^64
+    const bool bad = !(l_part <= kLMax) || !(__builtin_fabsf(osum) <= 3.0e38f);
+    if (__syncthreads_or(bad)) run(std::false_type{});
   }
 
   if constexpr (SPLIT) {

@@ -30,6 +30,52 @@ def test_premature_use_is_flagged(text):
     assert check_isa.check_text(text)
 
 
+# the read's wait is on one path only: the branch skips it
+BRANCH_SKIPS_WAIT = """
+kern:
+;;#ASMSTART
+	ds_read_b128 v[4:7], v1 offset:0
+;;#ASMEND
+	s_cbranch_scc1 .LBB0_2
+;;#ASMSTART
+	s_waitcnt lgkmcnt(0)
+;;#ASMEND
+.LBB0_2:
+	v_mov_b32_e32 v5, 0
+	s_endpgm
+"""
+# the wait is on both paths
+WAIT_ON_BOTH = BRANCH_SKIPS_WAIT.replace(""".LBB0_2:
+	v_mov_b32_e32 v5, 0""", """	s_branch .LBB0_3
+.LBB0_2:
+	s_waitcnt lgkmcnt(0)
+.LBB0_3:
+	v_mov_b32_e32 v5, 0""")
+# the use comes later in the text than the read, but control flow reaches it only
+# through a block (laid out after it) that waits
+LAYOUT = """
+kern:
+;;#ASMSTART
+	ds_read_b128 v[4:7], v1 offset:0
+;;#ASMEND
+	s_branch .LBB0_2
+.LBB0_1:
+	v_mov_b32_e32 v6, 0
+	s_endpgm
+.LBB0_2:
+;;#ASMSTART
+	s_waitcnt lgkmcnt(0)
+;;#ASMEND
+	s_branch .LBB0_1
+"""
+
+
+def test_control_flow():
+    assert check_isa.check_text(BRANCH_SKIPS_WAIT)
+    assert check_isa.check_text(WAIT_ON_BOTH) == []
+    assert check_isa.check_text(LAYOUT) == []
+
+
 def test_register_ranges():
     assert check_isa.regs_of("v[4:7], v1, s3") == {1, 4, 5, 6, 7}
 

@@ -559,6 +559,23 @@ def test_fwd_d128_long_scores_outgrow_first_tile(causal, N):
     _check_fwd_chunked(q, k, v, causal, 1.0, f"d128 N{N} rising scores", stress=True)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+def test_scores_overflowing_the_first_reference(causal, d):
+    """The 32-rows-per-wave forward first runs with tile 0's row maximum as a fixed
+    reference; scores that rise by about 173 in exp2 units along the keys overflow
+    float32 in that pass, and the workgroup must redo the rows with the moving reference."""
+    need_gpu()
+    N = 1024
+    q, k, v = inputs.gen_qkv((1, 2, N, d), "bf16", 94)
+    ramp = np.linspace(0.0, 30.0, N, dtype=np.float32)
+    q = inputs.bf16_round(q * 0.25)
+    q[..., 0] = 4.0  # score rise 4 * 30 = 120 (natural log units) along the keys
+    k[..., 0] = inputs.bf16_round(ramp)[None, None, :]
+    k = inputs.bf16_round(k)
+    check_fwd_full(q, k, v, causal, 1.0, "bf16", f"d{d} overflowing scores", stress=True)
+
+
 def test_peaky_scale():
     need_gpu()
     q, k, v = inputs.gen_qkv((2, 2, 512, 128), "bf16", 79)
