@@ -266,11 +266,11 @@ __device__ __forceinline__ u32x4 ds_read_b128_at(uint32_t addr) {
   return r;
 }
 
-// max(a, b, c) in one v_max3_f32 (no canonicalisation of the operands).
+// max(a, b, c): the compiler forms v_max3_f32 from it.  (Not inline asm: the
+// operands are often fresh matrix-core results, and only the compiler pads a
+// read of those with the wait states the hardware needs.)
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 // s_waitcnt lgkmcnt(0) followed by empty asm statements that redefine each of
