@@ -57,8 +57,8 @@ int check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, floa
   if ((unsigned long long)Nk * (unsigned long long)d * 2ull >= (1ull << 31)) return FA_ERR_BAD_SHAPE;
   if ((unsigned long long)Hq / Hkv * (unsigned long long)Nq > 0x7fffffffull) return FA_ERR_BAD_SHAPE;
   const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d);
-  if ((p.nwaves + 3) / 4 > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
-  if ((long long)B * Hq * Nq > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;  // one merge workgroup per query row
+  if (p.segments > (1LL << 30)) return FA_ERR_BAD_SHAPE;               // segment numbers (and pairs) fit in int32
+  if ((long long)B * Hq * Nq > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;  // up to one merge workgroup per query row
   if (causal != 0 && causal != 1) return FA_ERR_BAD_ARGUMENT;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_BAD_SCALE;
   return FA_OK;
@@ -238,7 +238,7 @@ int fa_decode(const void *q, const void *k, const void *v, const int *kv_lens, v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(kv_lens) & 3u) != 0)
     return FA_ERR_MISALIGNED;
-  hipError_t e = fa::launch_decode_bf16(q, k, v, kv_lens, o, lse, (float *)workspace, B, Hq, Hkv, Nq, Nk, d,
+  hipError_t e = fa::launch_decode_bf16(q, k, v, kv_lens, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d,
                                         causal == 1, scale, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

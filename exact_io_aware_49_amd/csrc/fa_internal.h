@@ -24,38 +24,39 @@ inline size_t bwd_partial_offset_floats(long long nqh, int N) {
   return ((bytes + 255) & ~(size_t)255) / sizeof(float);
 }
 
-// Attention of Nq query rows against a key/value cache (fa_decode): one wave
-// per (batch, K/V head, block of 32 query rows, key range of `chunk` keys);
-// the key range is split until there are about 2048 waves (at least 256 keys
-// each; 2048 long ranges beat 4096 shorter ones by 15% at B=16, 8 K/V heads,
-// an 8K cache: fewer partials to merge and less start-up per wave).  The workspace holds float32 partial O [B*Hq*Nq][nsplit][d] and,
-// 256-byte aligned after it, partial lse [B*Hq*Nq][nsplit].
+// Attention of Nq query rows against a key/value cache (fa_decode).  A
+// segment is one block of up to 32 query rows (the (query head, query) pairs
+// of one K/V head's group) of one sequence.  The decode kernel runs at most
+// kDecodeMaxWaves waves, each over an equal share of the list of 32-key tiles
+// of all segments, and writes a float32 partial result per (wave w, segment s)
+// pair it touches at slot w + s (distinct for every pair, below
+// kDecodeMaxWaves + segments).  Workspace layout (each part 256-byte aligned):
+// partial O [slots][rpb][d], partial lse [slots][rpb], and per segment the
+// first and last wave that handled it (int32 pairs).
+constexpr long long kDecodeMaxWaves = 2048;
+
 struct DecodePlan {
-  int nrb;                      // blocks of 32 query rows per (batch, K/V head)
-  int nsplit;                   // key ranges per row block
-  int chunk;                    // keys per range (multiple of 32)
-  long long nwaves;
-  size_t lpart_offset_floats;   // start of the lse partials in the workspace
-  size_t bytes;                 // workspace size
+  int nrb;                // blocks of 32 query rows per (sequence, K/V head)
+  int rpb;                // rows stored per partial: min(32, group * Nq)
+  long long segments;     // B * Hkv * nrb
+  size_t lpart_offset;    // byte offsets in the workspace
+  size_t segw_offset;
+  size_t bytes;           // workspace size
 };
 inline DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  (void)Nk;
   DecodePlan p;
   const long long rows = (long long)(Hq / Hkv) * Nq;
   p.nrb = (int)((rows + 31) / 32);
-  const long long base = (long long)B * Hkv * p.nrb;
-  long long s = (2048 + base - 1) / base;
-  const long long most = ((long long)Nk + 255) / 256;
-  if (s > most) s = most;
-  if (s < 1) s = 1;
-  const long long chunk = (((long long)Nk + s - 1) / s + 31) / 32 * 32;
-  s = ((long long)Nk + chunk - 1) / chunk;
-  p.nsplit = (int)s;
-  p.chunk = (int)chunk;
-  p.nwaves = base * s;
-  const size_t nrows = (size_t)B * (size_t)Hq * (size_t)Nq;
-  const size_t obytes = nrows * (size_t)s * (size_t)d * sizeof(float);
-  p.lpart_offset_floats = ((obytes + 255) & ~(size_t)255) / sizeof(float);
-  p.bytes = (p.lpart_offset_floats * sizeof(float) + nrows * (size_t)s * sizeof(float) + 255) & ~(size_t)255;
+  p.rpb = (int)(rows < 32 ? rows : 32);
+  p.segments = (long long)B * Hkv * p.nrb;
+  const size_t slots = (size_t)kDecodeMaxWaves + (size_t)p.segments;
+  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t obytes = align(slots * (size_t)p.rpb * (size_t)d * sizeof(float));
+  const size_t lbytes = align(slots * (size_t)p.rpb * sizeof(float));
+  p.lpart_offset = obytes;
+  p.segw_offset = obytes + lbytes;
+  p.bytes = p.segw_offset + align(2 * (size_t)p.segments * sizeof(int));
   return p;
 }
 
@@ -76,7 +77,7 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
                            int N, int d, bool causal, float scale, hipStream_t stream);
 
 hipError_t launch_decode_bf16(const void *q, const void *k, const void *v, const int *kv_lens, void *o, float *lse,
-                              float *ws, int B, int Hq, int Hkv, int Nq, int Nk, int d, bool causal, float scale,
+                              void *ws, int B, int Hq, int Hkv, int Nq, int Nk, int d, bool causal, float scale,
                               hipStream_t stream);
 
 }  // namespace fa

@@ -178,7 +178,7 @@ def gen_decode(B: int, hq: int, hkv: int, nq: int, nk: int, d: int, seed: int, m
 
 
 # Decode shapes (new query rows against a key/value cache) used by the parity
-# tests and the benchmark: one new token per sequence with 8 query heads per
+# tests and the benchmark: one new token per sequence with 4 query heads per
 # K/V head and ragged cache lengths (a 32-head, 8-K/V-head decoder at 8K
 # context), and four speculative tokens per sequence, causal, over a 4K cache.
 DECODE_CASES = {

@@ -191,11 +191,16 @@ FA_API int fa_bwd_gqa(const void *q, const void *k, const void *v, const void *o
  * Query i of sequence b sits at position L_b - Nq + i.  It attends to cache
  * rows j < L_b; with causal = 1 only to j <= L_b - Nq + i.  A query that sees
  * no row gets o = 0 and lse = -inf.
+ * Cache rows j >= L_b are never read (they may hold anything, NaN included).
  * Only FA_DTYPE_BF16 and d in {64, 128}.  The workspace (at least
- * fa_decode_workspace_size() bytes, 16-byte aligned) holds float32 partial
- * results: the cache is split into key ranges over many waves so that K and V
- * stream from HBM once at full bandwidth, and a second kernel merges the
- * ranges (lse = ln sum_s e^lse_s, o = sum_s e^(lse_s - lse) o_s).
+ * fa_decode_workspace_size() bytes, 16-byte aligned; its contents on entry do
+ * not matter) holds float32 partial results: the key tiles of all sequences
+ * and K/V heads are divided evenly over one wave per SIMD of the GPU so that K
+ * and V stream from HBM once at full bandwidth, and a second kernel merges the
+ * partial results (lse = ln sum_p e^lse_p, o = sum_p e^(lse_p - lse) o_p).
+ * The size depends on B, Hq, Hkv, Nq and d only (at most 2048 waves).  Results
+ * are bitwise reproducible on a given GPU model (the division over waves
+ * follows its compute-unit count).
  * fa_decode_workspace_size returns 0 for arguments fa_decode would reject.
  */
 FA_API size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype);

@@ -167,15 +167,23 @@ def test_decode_validation(kw, code):
 
 
 def test_decode_workspace_size():
-    # float32 partial O and lse per (query row, key range), 256-byte aligned
-    n = fa.fa_decode_workspace_size(16, 32, 8, 1, 8192, 128, 1)
-    rows = 16 * 32 * 1
-    assert n > 0 and n % 256 == 0
-    splits = (n - 256) // (rows * (128 + 1) * 4)
-    assert splits >= 1 and n >= rows * splits * (128 + 1) * 4
+    # float32 partial O [slots][rows][d] and lse [slots][rows] with slots = 2048 waves + segments,
+    # rows = min(32, Hq / Hkv * Nq), then two int32 per segment; each part 256-byte aligned
+    def expect(B, Hq, Hkv, Nq, d):
+        rows = Hq // Hkv * Nq
+        nrb = -(-rows // 32)
+        rpb = min(rows, 32)
+        segs = B * Hkv * nrb
+        al = lambda x: (x + 255) // 256 * 256
+        slots = 2048 + segs
+        return al(slots * rpb * d * 4) + al(slots * rpb * 4) + al(2 * segs * 4)
+    for args in [(16, 32, 8, 1, 8192, 128), (8, 16, 16, 4, 4096, 64), (2, 64, 1, 3, 100, 64), (1, 1, 1, 1, 1, 64)]:
+        B, Hq, Hkv, Nq, Nk, d = args
+        assert fa.fa_decode_workspace_size(*args, 1) == expect(B, Hq, Hkv, Nq, d), args
+    # the cache capacity does not enter
+    assert fa.fa_decode_workspace_size(16, 32, 8, 1, 100, 128, 1) == fa.fa_decode_workspace_size(16, 32, 8, 1, 8192, 128, 1)
     assert fa.fa_decode_workspace_size(16, 32, 8, 1, 8192, 128, 0) == 0
     assert fa.fa_decode_workspace_size(16, 32, 7, 1, 8192, 128, 1) == 0
-    assert fa.fa_decode_workspace_size(1, 1, 1, 1, 1, 64, 1) >= 64 * 4 + 4
 
 
 def fp8(**kw):

@@ -272,6 +272,49 @@ def test_decode_sweep(d, causal):
     _decode_check(q, k, v, None, causal, "decode full cache")
 
 
+def test_decode_long_sequences():
+    """Few long sequences, so each (sequence, K/V head) is split over many waves and the merge
+    combines hundreds of partials: one 64K-row cache, and two ragged causal ones."""
+    need_gpu()
+    q, k, v, _ = inputs.gen_decode(1, 8, 1, 1, 65536, 128, 1700)
+    _decode_check(q, k, v, None, False, "decode one 64K cache")
+    q, k, v, _ = inputs.gen_decode(2, 4, 1, 2, 30000, 64, 1701)
+    _decode_check(q, k, v, np.array([30000, 17], dtype=np.int32), True, "decode 30000 + 17 rows, causal")
+
+
+def test_decode_cache_rows_past_length_not_read():
+    """Cache rows at or past each sequence's length hold NaN: the output is bitwise the one with
+    finite rows there (those rows are never read), for lengths that end inside a tile."""
+    need_gpu()
+    for d, causal in [(128, False), (64, True)]:
+        q, k, v, _ = inputs.gen_decode(4, 8, 2, 3, 2000, d, 1710 + d)
+        lens = np.array([2000, 1001, 37, 0], dtype=np.int32)
+        _decode_check(q, k, v, lens, causal, f"decode ragged d={d}")
+        ld = torch.from_numpy(lens).to("cuda")
+        qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+        o1, l1 = fa.decode(qd, kd, vd, ld, causal=causal)
+        kn, vn = kd.clone(), vd.clone()
+        for b, n in enumerate(lens.tolist()):
+            kn[b, :, n:] = float("nan")
+            vn[b, :, n:] = float("nan")
+        o2, l2 = fa.decode(qd, kn, vn, ld, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"d={d}: output depends on rows past the length"
+
+
+def test_decode_bitwise_repeatable():
+    """Two calls on the 8K-cache decode workload give bitwise equal results."""
+    need_gpu()
+    c = inputs.DECODE_CASES["decode_b16hq32hkv8nk8192d128"]
+    q, k, v, lens = inputs.gen_decode(c["B"], c["hq"], c["hkv"], c["nq"], c["nk"], c["d"], c["seed"], c["min_len"])
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    ld = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to("cuda")
+    outs = [fa.decode(qd, kd, vd, ld) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
 # ------------------------------------------------------------------ head dim 256 (forward)
 
 @pytest.mark.parametrize("causal", [False, True])
