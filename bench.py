@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --calibrate-copy     (HBM counter calibration: a plain 512 MiB copy, 3 times)
+    python bench.py --sustain 5 --no-cpu-baseline   (adds the socket power and GFX clock that
+                                          5 s of back-to-back forwards, then backwards, settle at)
 
 --workload also accepts the shared-K/V-head cases (query heads grouped over
 fewer K/V heads), e.g. gqa_causal_b2hq32hkv4n2048d128; they are timed the same
@@ -338,6 +340,51 @@ def decode_main(a, name):
     return 0
 
 
+def sustained(fn, seconds: float):
+    """Run fn() back to back for `seconds` while sampling the socket power and the GFX
+    clocks with amd-smi every 0.5 s: the clock the chip holds under this load at its
+    power limit.  Returns medians over the samples taken after the first second."""
+    import subprocess
+    import threading
+
+    import torch
+
+    samples = []
+    stop = threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=10)
+                txt = r.stdout
+            except (OSError, subprocess.SubprocessError):
+                txt = ""
+            pw = re.findall(r"SOCKET_POWER:\s+(\d+)\s*W", txt)
+            ck = [int(x) for x in re.findall(r"GFX_\d+:\s+CLK:\s+(\d+)\s*MHz", txt)]
+            samples.append((time.perf_counter(), int(pw[0]) if pw else None, ck))
+            stop.wait(0.5)
+
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    calls = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        calls += 10
+    dt = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    late = [s for s in samples if s[0] - t0 >= 1.0 and s[1] is not None and s[2]]
+    if not late:
+        return {"ms_per_call": round(dt * 1e3 / calls, 4), "power_w": None, "gfx_mhz": None, "samples": 0}
+    return {"ms_per_call": round(dt * 1e3 / calls, 4),
+            "power_w": float(np.median([s[1] for s in late])),
+            "gfx_mhz": float(np.median([np.mean(s[2]) for s in late])),
+            "samples": len(late)}
+
+
 def calibrate_copy(mib: int = 512, reps: int = 3):
     """A plain device-to-device copy of a known size, for scaling the HBM byte counters
     (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE): each copy reads and writes exactly
@@ -361,6 +408,9 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--sustain", type=float, default=0.0,
+                    help="after the timed steps, run the forward and then the backward back to back for this many "
+                         "seconds each, sampling socket power and GFX clocks with amd-smi (reported under 'sustained')")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 512 MiB device copy three times (HBM counter calibration)")
     a = ap.parse_args(argv)
@@ -499,6 +549,8 @@ def main(argv=None):
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if a.sustain > 0:
+        line["sustained"] = {"fwd": sustained(fwd, a.sustain), "bwd": sustained(bwd, a.sustain)}
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
     print(json.dumps(line), flush=True)
