@@ -174,22 +174,24 @@ class _Case:
 
 
 def _time_steps(step, a, stream):
-    """a.warmup untimed calls, then a.steps timed ones: (wall ms per step, mean ms between
-    HIP events recorded on `stream` around each call)."""
+    """a.warmup untimed calls, then a.steps timed ones back to back: (wall ms per step, ms per
+    step between two HIP events recorded on `stream` before the first and after the last call).
+    No events between the calls: for launches of tens of microseconds, an event record per call
+    would add its own time to every step."""
     import torch
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(a.steps):
-        ev[i][0].record(stream)
+    e0.record(stream)
+    for _ in range(a.steps):
         step()
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall * 1e3 / a.steps, float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    return wall * 1e3 / a.steps, e0.elapsed_time(e1) / a.steps
 
 
 def fp8_main(a, name):
