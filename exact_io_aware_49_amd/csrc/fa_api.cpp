@@ -96,6 +96,25 @@ void *scratch_on_current_device() {
 
 }  // namespace
 
+namespace fa {
+
+// Compute units of the current device, looked up once per device.
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace fa
+
 extern "C" {
 
 int fa_version(void) { return kVersion; }

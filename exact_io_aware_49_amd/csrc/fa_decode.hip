@@ -626,21 +626,6 @@ fa_decode_merge_wide_kernel(const float *__restrict__ Opart, const float *__rest
   if (lane == 0) LSE[row] = lse_out;
 }
 
-// Compute units of the current device (looked up once per device).
-int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64) {
-    const int c = cached[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch(const void *q, const void *k, const void *v, const int *kv_lens, void *o, float *lse, void *ws,
                   int B, int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t stream) {

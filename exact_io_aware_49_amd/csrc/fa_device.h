@@ -142,6 +142,31 @@ __device__ __forceinline__ void map_block(int bid, int nqb, int nbh, bool causal
   qb = id % nqb;
 }
 
+// map_block for causal launches whose workgroups are all resident at once.
+// Each XCD hands its workgroups to its compute units in rounds of `round`
+// (its CU count), the same CU order every round, so a CU runs the workgroups at
+// positions p, p + round, p + 2 round, ... of the XCD's list.  Heaviest first in
+// every round would give the first CUs the heaviest block of every round; here
+// the odd rounds run lightest first, so the blocks a CU holds together sum to
+// about the same number of key tiles everywhere (a snake order).  round = 0, or
+// a grid that does not split evenly over the XCDs, gives map_block's order.
+__device__ __forceinline__ void map_block_balanced(int bid, int nqb, int nbh, int round, int &bh, int &qb) {
+  const int total = nqb * nbh;
+  const int per_xcd = total >> 3;
+  if (round <= 0 || (total & 7) != 0 || per_xcd % nqb != 0) {
+    map_block(bid, nqb, nbh, true, bh, qb);
+    return;
+  }
+  const int x = bid & 7;
+  int local = bid >> 3;
+  const int r = local / round;
+  const int pos = local - r * round;
+  if ((r & 1) && (r + 1) * round <= per_xcd) local = r * round + (round - 1 - pos);
+  const int heads_here = per_xcd / nqb;
+  bh = x * heads_here + local % heads_here;
+  qb = nqb - 1 - local / heads_here;
+}
+
 // ---- staging of 4-row x 8-column bf16 blocks into LDS -----------------------
 // A block is rows r0..r0+3, columns 8g..8g+7 of a row-major [nrows][ld] bf16
 // matrix: four 16-byte vectors, one per row.  Rows >= nrows read as zero.

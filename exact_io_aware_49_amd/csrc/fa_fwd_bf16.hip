@@ -44,7 +44,13 @@
 //     under the previous chunk's matrix products.
 //   * Causal: tiles entirely above the diagonal are never loaded; a wave whose
 //     rows are all above a tile skips its math; only diagonal and ragged tiles
-//     pay for masking.
+//     pay for masking.  Heaviest row blocks are dispatched first; when the
+//     whole grid is resident at once (B8 H12 N1024 d64: 768 workgroups, three
+//     per CU) the odd dispatch rounds go lightest first, so each CU's three
+//     blocks sum to 24-30 key tiles instead of 20-34 (per-workgroup timestamps;
+//     that launch 27.1 -> 25.5 us).
+#include <atomic>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -97,7 +103,7 @@ template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(64 * FwdCfg<D>::NWV, SPLIT ? 2 : ((D == 256) ? 1 : (D == 64) ? 3 : 8 / FwdCfg<D>::NWV))
 fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                    const __bf16 *__restrict__ V, __bf16 *__restrict__ O, float *__restrict__ LSE,
-                   int N, int nbh, int group, float scale_log2e) {
+                   int N, int nbh, int group, float scale_log2e, int xcd_round) {
   using C = FwdCfg<D>;
   static_assert(!SPLIT || (CAUSAL && C::NWV == 4), "the key split is built for 4-wave causal launches");
   constexpr int TB = C::TILE_BYTES;
@@ -121,7 +127,8 @@ fa_fwd_bf16_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
 
   const int nqb = (N + BRW - 1) / BRW;
   int bh, qb;
-  map_block(blockIdx.x, nqb, nbh, CAUSAL, bh, qb);
+  if (CAUSAL && xcd_round > 0) map_block_balanced(blockIdx.x, nqb, nbh, xcd_round, bh, qb);
+  else map_block(blockIdx.x, nqb, nbh, CAUSAL, bh, qb);
 
   const size_t head_off = (size_t)bh * (size_t)N * D;          // query head: Q, O
   const size_t kv_off = (size_t)(bh / group) * (size_t)N * D;  // its K/V head (group query heads share one)
@@ -532,9 +539,23 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
   const int nqb = (N + br - 1) / br;
   const long long blocks = (long long)nqb * nbh;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // causal grids that are resident all at once: the snake order of map_block_balanced
+  int xcd_round = 0;
+  if (CAUSAL && !SPLIT) {
+    static std::atomic<int> per_cu{0};  // workgroups of this kernel one CU holds
+    int r = per_cu.load(std::memory_order_relaxed);
+    if (r == 0) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>, 64 * C::NWV, 0) !=
+              hipSuccess || r < 1)
+        r = 1;
+      per_cu.store(r, std::memory_order_relaxed);
+    }
+    const int cus = cu_count();
+    if (cus % 8 == 0 && blocks % 8 == 0 && blocks <= (long long)r * cus) xcd_round = cus / 8;
+  }
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3((unsigned)blocks), dim3(64 * C::NWV), 0, stream,
                      (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, N, nbh, group,
-                     scale * kLog2e);
+                     scale * kLog2e, xcd_round);
   return hipGetLastError();
 }
 

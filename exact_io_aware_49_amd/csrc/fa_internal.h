@@ -60,6 +60,10 @@ inline DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   return p;
 }
 
+// Compute units of the current device (looked up once per device; 256 if the
+// query fails).
+int cu_count();
+
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
 // Arguments are already validated by the C ABI layer.  H is the number of
 // query heads; `group` query heads share one K/V head (H / group K/V heads).

@@ -536,6 +536,20 @@ def test_fwd_d64_causal_key_split():
     check_fwd_full(q, k, v, True, 0.125, "bf16", "unsplit B=1 H=257 N=128")
 
 
+def test_fwd_causal_resident_grid_orders():
+    """Causal launches whose whole grid is resident at once take the snake dispatch order
+    (odd rounds of each XCD's list lightest first).  Every output row against the oracle for
+    grids of three full rounds per XCD (B8 H12 N1024 at d = 32, and B8 H12 N1000: ragged last
+    block), two full rounds and a partial one that keeps the forward order (B8 H10 N1024 d64),
+    one full and one partial round (B4 H12 N1024 d64), and a grid whose share per XCD is not
+    a whole number of heads (B3 H5 N1024 d64: the plain order)."""
+    need_gpu()
+    cases = [(8, 12, 1024, 32), (8, 12, 1000, 64), (8, 10, 1024, 64), (4, 12, 1024, 64), (3, 5, 1024, 64)]
+    for i, (B, H, N, d) in enumerate(cases):
+        q, k, v = inputs.gen_qkv((B, H, N, d), "bf16", 2300 + 11 * i)
+        check_fwd_full(q, k, v, True, d ** -0.5, "bf16", f"resident causal grid B={B} H={H} N={N} d={d}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_sweep(d, causal):
