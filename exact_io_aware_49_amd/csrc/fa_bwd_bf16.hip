@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(64 * dq_waves<D>(), (D == 256) ? 1 : 8 / dq_wa
 fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                  const __bf16 *__restrict__ Og, const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
                  __bf16 *__restrict__ dQ, float *__restrict__ Dsum, float *__restrict__ Lse2, int N,
-                 int group, float scale_log2e, float scale) {
+                 int group, float scale_log2e, float scale, int xcd_round) {
   using C = BwdCfg<D>;
   constexpr int TB = C::TB;
   constexpr int RB = C::RB;
@@ -196,7 +196,9 @@ fa_bwd_dq_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, con
   const int nqb = (N + BR - 1) / BR;
   const int nbh = gridDim.x / nqb;
   int bh, qb;
-  map_block(blockIdx.x, nqb, nbh, CAUSAL, bh, qb);  // same-head blocks share an XCD's L2
+  // same-head blocks share an XCD's L2
+  if (CAUSAL && xcd_round > 0) map_block_balanced(blockIdx.x, nqb, nbh, xcd_round, bh, qb);
+  else map_block(blockIdx.x, nqb, nbh, CAUSAL, bh, qb);
   const size_t head_off = (size_t)bh * N * D;
   const int q0 = qb * BR;
   const int qw0 = q0 + 32 * wave;
@@ -319,7 +321,7 @@ __global__ void __launch_bounds__(256, (D == 256) ? 1 : (D == 96) ? 2 : 3)
 fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                    const __bf16 *__restrict__ dO, const float *__restrict__ Dsum, const float *__restrict__ Lse2,
                    __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, float *__restrict__ part, int N, int group,
-                   int nsplit, float scale_log2e, float scale) {
+                   int nsplit, float scale_log2e, float scale, int xcd_round) {
   using C = BwdCfg<D>;
   constexpr int TB = C::TB;
   constexpr int RB = C::RB;
@@ -335,7 +337,9 @@ fa_bwd_dkdv_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, c
   const int nkb = (N + BKV - 1) / BKV;
   const int nkvh = gridDim.x / (nkb * nsplit);  // K/V heads
   int vh, rb;
-  map_block(blockIdx.x, nkb, nkvh * nsplit, CAUSAL, vh, rb);  // same-head blocks share an XCD's L2
+  // same-head blocks share an XCD's L2
+  if (CAUSAL && xcd_round > 0) map_block_balanced(blockIdx.x, nkb, nkvh * nsplit, xcd_round, vh, rb);
+  else map_block(blockIdx.x, nkb, nkvh * nsplit, CAUSAL, vh, rb);
   // the query heads of a K/V head's group may be split over nsplit workgroups,
   // each writing a float32 partial dK/dV that a reduction kernel sums
   const int bh = vh / nsplit;
@@ -492,7 +496,7 @@ __global__ void __launch_bounds__(512, 1)
 fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                    const __bf16 *__restrict__ dO, const float *__restrict__ Dsum, const float *__restrict__ Lse2,
                    __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, float *__restrict__ part, int N, int group,
-                   int nsplit, float scale_log2e, float scale) {
+                   int nsplit, float scale_log2e, float scale, int xcd_round) {
   using C = BwdCfg<D>;
   constexpr int TB = C::TB;
   constexpr int RB = C::RB;
@@ -513,7 +517,9 @@ fa_bwd_dkdv_pair_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__
   const int nkb = (N + BKV - 1) / BKV;
   const int nkvh = gridDim.x / (nkb * nsplit);  // K/V heads
   int vh, rb;
-  map_block(blockIdx.x, nkb, nkvh * nsplit, CAUSAL, vh, rb);  // same-head blocks share an XCD's L2
+  // same-head blocks share an XCD's L2
+  if (CAUSAL && xcd_round > 0) map_block_balanced(blockIdx.x, nkb, nkvh * nsplit, xcd_round, vh, rb);
+  else map_block(blockIdx.x, nkb, nkvh * nsplit, CAUSAL, vh, rb);
   // the query heads of a K/V head's group may be split over nsplit workgroups,
   // each writing a float32 partial dK/dV that a reduction kernel sums
   const int bh = vh / nsplit;
@@ -755,33 +761,41 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
   float *dsum = ws;
   float *lse2 = ws + (size_t)nbh * N;
   float *part = (nsplit > 1) ? ws + bwd_partial_offset_floats(nbh, N) : nullptr;
+  // causal grids the device holds all at once: the snake order of map_block_balanced
+  int rq = 0, rk = 0;
+  if constexpr (CAUSAL) {
+    static std::atomic<int> per_cu_q{0}, per_cu_k{0};
+    rq = snake_round(fa_bwd_dq_kernel<D, CAUSAL>, 64 * dq_waves<D>(), gq, per_cu_q);
+    if constexpr (D == 128) rk = snake_round(fa_bwd_dkdv_pair_kernel<D, CAUSAL>, 512, gk, per_cu_k);
+    else if constexpr (D != 256) rk = snake_round(fa_bwd_dkdv_kernel<D, CAUSAL>, 256, gk, per_cu_k);
+  }
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)gq), dim3(64 * dq_waves<D>()), 0, stream,
                      (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)o,
-                     (const __bf16 *)dout, lse, (__bf16 *)dq, dsum, lse2, N, group, c, scale);
+                     (const __bf16 *)dout, lse, (__bf16 *)dq, dsum, lse2, N, group, c, scale, rq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (D != 128 && D != 256)
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(256), 0, stream,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
                        (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
-                       nsplit, c, scale);
+                       nsplit, c, scale, rk);
   else if constexpr (D == 256) {
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, 1>), dim3((unsigned)gk), dim3(256), 0, stream,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
                        (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
-                       nsplit, c, scale);
+                       nsplit, c, scale, rk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL, 2>), dim3((unsigned)gk), dim3(256), 0, stream,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
                        (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
-                       nsplit, c, scale);
+                       nsplit, c, scale, rk);
   }
   else
     hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)gk), dim3(512), 0, stream,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (const __bf16 *)dout,
                        (const float *)dsum, (const float *)lse2, (__bf16 *)dk, (__bf16 *)dv, part, N, group,
-                       nsplit, c, scale);
+                       nsplit, c, scale, rk);
   if (nsplit == 1) return hipGetLastError();
   e = hipGetLastError();
   if (e != hipSuccess) return e;

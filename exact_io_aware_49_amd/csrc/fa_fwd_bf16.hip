@@ -49,8 +49,6 @@
 //     per CU) the odd dispatch rounds go lightest first, so each CU's three
 //     blocks sum to 24-30 key tiles instead of 20-34 (per-workgroup timestamps;
 //     that launch 27.1 -> 25.5 us).
-#include <atomic>
-
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -542,16 +540,8 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, float *l
   // causal grids that are resident all at once: the snake order of map_block_balanced
   int xcd_round = 0;
   if (CAUSAL && !SPLIT) {
-    static std::atomic<int> per_cu{0};  // workgroups of this kernel one CU holds
-    int r = per_cu.load(std::memory_order_relaxed);
-    if (r == 0) {
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>, 64 * C::NWV, 0) !=
-              hipSuccess || r < 1)
-        r = 1;
-      per_cu.store(r, std::memory_order_relaxed);
-    }
-    const int cus = cu_count();
-    if (cus % 8 == 0 && blocks % 8 == 0 && blocks <= (long long)r * cus) xcd_round = cus / 8;
+    static std::atomic<int> per_cu{0};
+    xcd_round = snake_round(fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>, 64 * C::NWV, blocks, per_cu);
   }
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3((unsigned)blocks), dim3(64 * C::NWV), 0, stream,
                      (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, N, nbh, group,

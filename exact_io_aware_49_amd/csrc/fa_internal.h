@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 namespace fa {
 
 // Backward with query heads sharing K/V heads: the workgroups that own a block
@@ -63,6 +65,23 @@ inline DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
 // Compute units of the current device (looked up once per device; 256 if the
 // query fails).
 int cu_count();
+
+// Round length for map_block_balanced: a causal grid of `blocks` workgroups of
+// `kernel` that the device holds all at once (at most the kernel's resident
+// workgroups per CU times the CU count, and whole rounds over the 8 XCDs) gets
+// its XCD's CU count; any other grid gets 0 (map_block's order).  `per_cu`
+// caches the kernel's resident workgroups per CU (0 = not looked up yet).
+template <typename Kernel>
+int snake_round(Kernel kernel, int threads, long long blocks, std::atomic<int> &per_cu) {
+  int r = per_cu.load(std::memory_order_relaxed);
+  if (r == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, kernel, threads, 0) != hipSuccess || r < 1) r = 1;
+    per_cu.store(r, std::memory_order_relaxed);
+  }
+  const int cus = cu_count();
+  if (cus % 8 != 0 || blocks % 8 != 0 || blocks > (long long)r * cus) return 0;
+  return cus / 8;
+}
 
 // Each launcher enqueues its kernels on `stream` and returns hipGetLastError().
 // Arguments are already validated by the C ABI layer.  H is the number of
