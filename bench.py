@@ -52,9 +52,11 @@ DEFAULT_WORKLOAD = "fwd_encoder_b4h16n4096d128"
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_bwd_encoder_b4h16n4096d128_hbm_traffic.md")
-BWD_SOURCES = ["exact_io_aware_49_amd/csrc/fa_bwd_bf16.hip", "exact_io_aware_49_amd/csrc/fa_device.h"]
+BWD_SOURCES = ["exact_io_aware_49_amd/csrc/fa_bwd_bf16.hip", "exact_io_aware_49_amd/csrc/fa_device.h",
+               "exact_io_aware_49_amd/csrc/fa_map.h"]
 FP8_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fa_fwd_fp8_b4h16n4096d128_hbm_traffic.md")
-FP8_SOURCES = ["exact_io_aware_49_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_49_amd/csrc/fa_device.h"]
+FP8_SOURCES = ["exact_io_aware_49_amd/csrc/fa_fwd_fp8.hip", "exact_io_aware_49_amd/csrc/fa_device.h",
+               "exact_io_aware_49_amd/csrc/fa_map.h"]
 DEC_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_b16hq32hkv8nk8192d128_kernel_trace.md")
 DEC_SOURCES = ["exact_io_aware_49_amd/csrc/fa_decode.hip", "exact_io_aware_49_amd/csrc/fa_device.h",
                "exact_io_aware_49_amd/csrc/fa_internal.h"]

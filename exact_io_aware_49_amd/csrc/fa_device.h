@@ -17,6 +17,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "fa_map.h"
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -109,62 +111,6 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_fl
 // (scores times values) wants for its B operand.
 __device__ __forceinline__ int swap_bits23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
-// Map the linear workgroup id to (batch*head, row block) for grids of
-// nbh * nqb workgroups.  Workgroups are
-// dispatched round-robin over the 8 XCDs; grouping consecutive ids of one XCD
-// onto the same heads keeps a head's K/V in that XCD's L2.  Causal launches
-// put the highest row blocks first (the heaviest for a query-block owner).
-__device__ __forceinline__ void map_block(int bid, int nqb, int nbh, bool causal, int &bh, int &qb) {
-  const int total = nqb * nbh;
-  int id = bid;
-  if ((total & 7) == 0) {
-    const int per_xcd = total >> 3;
-    id = (bid & 7) * per_xcd + (bid >> 3);
-  }
-  if (causal) {
-    const int per_xcd = ((total & 7) == 0) ? (total >> 3) : total;
-    const int base = (id / per_xcd) * per_xcd;
-    const int local = id - base;
-    if (per_xcd % nqb == 0) {
-      const int heads_here = per_xcd / nqb;
-      const int qrank = local / heads_here;
-      bh = base / nqb + (local % heads_here);
-      qb = nqb - 1 - qrank;
-      return;
-    }
-    bh = id / nqb;
-    qb = nqb - 1 - (id % nqb);
-    return;
-  }
-  bh = id / nqb;
-  qb = id % nqb;
-}
-
-// map_block for causal launches whose workgroups are all resident at once.
-// Each XCD hands its workgroups to its compute units in rounds of `round`
-// (its CU count), the same CU order every round, so a CU runs the workgroups at
-// positions p, p + round, p + 2 round, ... of the XCD's list.  Heaviest first in
-// every round would give the first CUs the heaviest block of every round; here
-// the odd rounds run lightest first, so the blocks a CU holds together sum to
-// about the same number of key tiles everywhere (a snake order).  round = 0, or
-// a grid that does not split evenly over the XCDs, gives map_block's order.
-__device__ __forceinline__ void map_block_balanced(int bid, int nqb, int nbh, int round, int &bh, int &qb) {
-  const int total = nqb * nbh;
-  const int per_xcd = total >> 3;
-  if (round <= 0 || (total & 7) != 0 || per_xcd % nqb != 0) {
-    map_block(bid, nqb, nbh, true, bh, qb);
-    return;
-  }
-  const int x = bid & 7;
-  int local = bid >> 3;
-  const int r = local / round;
-  const int pos = local - r * round;
-  if ((r & 1) && (r + 1) * round <= per_xcd) local = r * round + (round - 1 - pos);
-  const int heads_here = per_xcd / nqb;
-  bh = x * heads_here + local % heads_here;
-  qb = nqb - 1 - local / heads_here;
 }
 
 // ---- staging of 4-row x 8-column bf16 blocks into LDS -----------------------
