@@ -410,10 +410,13 @@ fa_decode_merge_kernel(const float *__restrict__ Opart, const float *__restrict_
 #pragma unroll
   for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
   float lse_out = -INFINITY;
+  // the segment's first and last wave, loaded together with the sequence length
+  // (one round trip; for an empty sequence they are stale and go unused)
+  const int sw0 = segw[2 * s_idx], sw1 = segw[2 * s_idx + 1];
   if (seq_len(kv_lens, b, Nk) > 0) {
     // (clamped, so that no value can send a read outside the partial slots)
-    const int wf = min(max(segw[2 * s_idx], 0), W - 1);
-    const int wl = min(max(segw[2 * s_idx + 1], wf), W - 1);
+    const int wf = min(max(sw0, 0), W - 1);
+    const int wl = min(max(sw1, wf), W - 1);
     const int np = wl - wf + 1;
     const float *lp = Lpart + ((long long)wf + s_idx) * rpb + rin;
     // each slot group: online-softmax merge of its slots (loads of all its
@@ -522,11 +525,14 @@ fa_decode_merge_wide_kernel(const float *__restrict__ Opart, const float *__rest
 #pragma unroll
   for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
   float mg = -INFINITY, sg = 0.f;
+  // the segment's first and last wave, loaded together with the sequence length
+  // (one round trip; for an empty sequence they are stale and go unused)
+  const int sw0 = segw[2 * s_idx], sw1 = segw[2 * s_idx + 1];
   const bool any_rows = seq_len(kv_lens, b, Nk) > 0;
   if (any_rows) {
     // (clamped, so that no value can send a read outside the partial slots)
-    const int wf = min(max(segw[2 * s_idx], 0), W - 1);
-    const int wl = min(max(segw[2 * s_idx + 1], wf), W - 1);
+    const int wf = min(max(sw0, 0), W - 1);
+    const int wl = min(max(sw1, wf), W - 1);
     const int np = wl - wf + 1;
     const float *lp = Lpart + ((long long)wf + s_idx) * rpb + rin;
     for (int p0 = grp; p0 < np; p0 += 128) {
