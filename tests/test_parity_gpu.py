@@ -218,6 +218,22 @@ def test_workload_bwd_causal():
     assert np.abs(dv.sum(axis=2) - do.astype(np.float64).sum(axis=2)).max() < 0.5
 
 
+def test_bwd_causal_resident_grid_orders():
+    """Causal backward launches whose dQ and dK/dV grids are resident at once take the snake
+    dispatch order.  The GPT-2 shape (B8 H12 N1024 d64: three full rounds in both kernels) on every
+    head against the oracle; two full rounds and a partial one (B8 H10 N1024 d64) and d = 32
+    (B8 H12 N1024) on a spread of heads, gradient identities on all."""
+    need_gpu()
+    cases = [((8, 12, 1024, 64), None), ((8, 10, 1024, 64), 16), ((8, 12, 1024, 32), 16)]
+    for i, ((B, H, N, d), nheads) in enumerate(cases):
+        q, k, v, do = inputs.gen_qkv((B, H, N, d), "bf16", 2400 + 13 * i, with_do=True)
+        allh = [(b, h) for b in range(B) for h in range(H)]
+        heads = allh if nheads is None else allh[:: max(1, len(allh) // nheads)]
+        dq, dk, dv = check_bwd_heads(q, k, v, do, True, d ** -0.5, heads, f"resident causal grid B={B} H={H} d={d}")
+        assert np.abs(dk.sum(axis=2)).max() < 0.5
+        assert np.abs(dv.sum(axis=2) - do.astype(np.float64).sum(axis=2)).max() < 0.5
+
+
 def test_bwd_encoder_shape():
     """The backward at the non-causal d=128 encoder shape (the benchmark's step)."""
     need_gpu()
