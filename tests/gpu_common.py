@@ -50,6 +50,12 @@ def errors(got, ref):
     return mx, rel
 
 
+# Every bf16 tensor gated here is also checked with allclose(atol=2e-2, rtol=1e-2)
+# (elementwise |gpu - ref| <= 2e-2 + 1e-2 |ref|).  That is reported, not gated: the
+# test session prints the count and names (tests/conftest.py).
+ALLCLOSE = {"pass": 0, "fail": []}
+
+
 def assert_close(name, got, ref, dtype, lse=False, magnitude_scaled=False):
     """Gate one output tensor.  `magnitude_scaled` (stress inputs only, never the
     named workloads) multiplies the absolute bound by max(1, max|ref|), because a
@@ -57,6 +63,11 @@ def assert_close(name, got, ref, dtype, lse=False, magnitude_scaled=False):
     mx, rel = errors(got, ref)
     if not np.all(np.isfinite(got)):
         raise AssertionError(f"{name}: non-finite values")
+    if dtype != "f32":
+        if np.allclose(np.asarray(got, np.float64), np.asarray(ref, np.float64), atol=TOL_BF16_ABS, rtol=TOL_BF16_REL):
+            ALLCLOSE["pass"] += 1
+        else:
+            ALLCLOSE["fail"].append(name)
     if dtype == "f32":
         assert mx <= TOL_F32_ABS, f"{name}: max abs err {mx:.3e} > {TOL_F32_ABS}"
     else:
