@@ -50,12 +50,14 @@ def common_flags(debug: bool):
     return flags
 
 
-# Per-source code-generation flags.  The decode kernel runs one wave per SIMD,
-# where the compiler otherwise keeps its matrix accumulators in AGPRs and copies
-# all of them to VGPRs and back on every key tile; the VGPR form of the MFMA
-# instructions removes those copies (same results, 2-8% faster).
+# Per-source code-generation flags.  The decode kernel and the 64-row forward
+# run one wave per SIMD, where the compiler otherwise keeps matrix results in
+# AGPRs and copies them to VGPRs for the vector code on every key tile; the
+# VGPR form of the MFMA instructions removes those copies (same results; decode
+# 2-8% faster, the 64-row forward 1%).
 SOURCE_FLAGS = {
     "fa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa_fwd_bf16_r64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
