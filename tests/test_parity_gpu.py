@@ -301,6 +301,23 @@ def test_decode_long_sequences():
     _decode_check(q, k, v, np.array([30000, 17], dtype=np.int32), True, "decode 30000 + 17 rows, causal")
 
 
+def test_decode_many_sequences():
+    """More than 64 sequences: the kernel reads the cache lengths 64 sequences at a time while
+    it sizes the tile list, finds each wave's first tile and moves from sequence to sequence.
+    Ragged lengths with empty caches among them; a run of empty sequences across a 64-boundary."""
+    need_gpu()
+    for i, (B, hq, hkv, nq, nk, d, causal) in enumerate([(150, 8, 2, 1, 512, 128, False),
+                                                          (97, 4, 4, 3, 300, 64, True),
+                                                          (200, 2, 1, 1, 40, 64, False)]):
+        rng = np.random.Generator(np.random.PCG64(1750 + i))
+        lens = rng.integers(0, nk + 1, size=B).astype(np.int32)
+        lens[rng.random(B) < 0.1] = 0
+        lens[60:70] = 0
+        lens[B - 1] = nk
+        q, k, v, _ = inputs.gen_decode(B, hq, hkv, nq, nk, d, 1760 + i)
+        _decode_check(q, k, v, lens, causal, f"decode B={B} Hq={hq} Hkv={hkv} Nq={nq} Nk={nk} d={d}")
+
+
 def test_decode_cache_rows_past_length_not_read():
     """Cache rows at or past each sequence's length hold NaN: the output is bitwise the one with
     finite rows there (those rows are never read), for lengths that end inside a tile."""
